@@ -1,0 +1,245 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache attention library (libpkv.so).
+ *
+ * The method: a request's keys and values are logically contiguous but stored
+ * in fixed 16-token blocks scattered through one preallocated pool, and a
+ * block table maps each logical block to a physical one
+ * ["(2) vLLM Internals: From PagedAttention to Removing PagedAttention",
+ * section 1.1 "The Analogy"; "My Understanding of vLLM and PagedAttention",
+ * sections "1. Logical Blocks", "2. Physical Blocks", "3. Block Table"].
+ * The worker keeps the table as a dense int32 tensor
+ * [rows, max_blocks_per_row] and the new tokens' destinations as an int64 slot
+ * mapping, both indexed by the kernels themselves ["vLLM: what PagedAttention
+ * turned into", section "The problem PagedAttention was actually solving"];
+ * the attention kernels gather the paged KV inside the kernel ["(2) vLLM
+ * Internals ...", section 4.1 "Why It Could Go"].
+ *
+ * Conventions
+ *  - Every function returns an int: PKV_OK (0) or a negative PKV_ERR_* code.
+ *    pkv_last_error() then holds a message (per thread).
+ *  - Block size is fixed at PKV_BLOCK_SIZE = 16 tokens.
+ *  - Pool layout (one tensor for K, one for V, row-major, contiguous):
+ *        [num_blocks][num_kv_heads][16][head_dim]
+ *    Token position p of a sequence whose logical block p/16 is physical
+ *    block b lives at slot b*16 + p%16, i.e. at [b][h][p%16][:] for head h.
+ *  - Block 0 is the null block: never handed out, used as table padding.
+ *  - Device entry points only enqueue work on the given stream (a hipStream_t,
+ *    NULL = the null stream); they never synchronise with the host and
+ *    allocate no device memory, so they may be captured in a HIP graph.
+ *    Arguments are checked on the host before any launch; a rejected call
+ *    enqueues nothing. Device-resident values (slots, block ids, context
+ *    lengths) are range-checked inside the kernels: out-of-range entries are
+ *    skipped or clamped as documented per call, never dereferenced.
+ *  - Ownership: the caller owns every buffer (pools, queries, outputs, tables,
+ *    slot mappings, workspaces) and the stream. The library keeps no device
+ *    pointer past a call. An allocator handle is host-only, owned by the
+ *    caller and not thread-safe (callers serialise access to one handle).
+ *  - dtype: PKV_F32 (float32) or PKV_BF16 (bfloat16, raw 16-bit storage);
+ *    head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with at most
+ *    16 query heads per KV head.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* a null pointer, a negative size, a bad id  */
+  PKV_ERR_UNSUPPORTED = -2,   /* dtype / head_dim / group size not built    */
+  PKV_ERR_OUT_OF_BLOCKS = -3, /* the pool cannot satisfy the request        */
+  PKV_ERR_NO_SUCH_SEQ = -4,   /* an unknown sequence id                     */
+  PKV_ERR_SEQ_EXISTS = -5,    /* a sequence id already in use               */
+  PKV_ERR_WORKSPACE = -6,     /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -7            /* the HIP runtime reported an error          */
+};
+
+enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Fixed description of a status code. */
+const char* pkv_strerror(int code);
+/* Library version, major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Host allocator: the KV-cache manager that allocates blocks, frees them and
+ * maintains block tables ["My Understanding of vLLM and PagedAttention",
+ * "vLLM System Architecture", item "2. KV-Cache Manager"]. Host memory only.
+ *
+ * Policy ["vLLM: what PagedAttention turned into", section "The block pool,
+ * and the two tricks in it"]: the free queue starts as 0, 1, ..., NB-1 and
+ * its first block, 0, is burned as the null block; allocation takes blocks
+ * from the front; a sequence is released tail first and every block whose
+ * refcount reaches zero goes back to the front in that order (so the tail is
+ * reused first). Sequences share blocks by reference counting; appending to
+ * a sequence whose last block is partially filled and shared first moves it
+ * to a private copy and reports the (source, destination) pair for
+ * pkv_copy_blocks ["(2) vLLM Internals ...", 1.2 "Three Direct Wins"].
+ * Every call is all-or-nothing: on failure the allocator is unchanged.
+ */
+typedef struct pkv_allocator pkv_allocator;
+
+typedef struct pkv_stats {
+  int32_t num_seqs;        /* live sequences                                 */
+  int32_t used_blocks;     /* blocks with refcount > 0                       */
+  int32_t free_blocks;     /* blocks in the free queue                       */
+  int32_t shared_blocks;   /* blocks with refcount > 1                       */
+  int64_t logical_tokens;  /* sum of sequence lengths (shared tokens counted per sequence) */
+  int64_t stored_tokens;   /* distinct token slots holding state             */
+  double utilisation;      /* stored_tokens / (16 * used_blocks), 0 if none  */
+} pkv_stats;
+
+/* Create an allocator over num_blocks blocks (>= 2: block 0 is the null
+ * block). *out receives the handle. */
+int pkv_allocator_create(int32_t num_blocks, pkv_allocator** out);
+/* Destroy a handle (NULL is accepted). */
+int pkv_allocator_destroy(pkv_allocator* a);
+/* Replace the free-queue order by order[0..n-1], which must be a permutation
+ * of 1..num_blocks-1 (n = num_blocks-1); only while no sequence exists.
+ * Used to place blocks at random physical positions. */
+int pkv_allocator_set_free_order(pkv_allocator* a, const int32_t* order, int32_t n);
+/* Create an empty sequence. PKV_ERR_SEQ_EXISTS if the id is taken. */
+int pkv_seq_add(pkv_allocator* a, int64_t seq_id);
+/* Append n_tokens >= 0 tokens to one sequence. out_slots[n_tokens] receives
+ * each new token's slot (int64, block*16 + offset). out_cow_pairs receives up
+ * to max_pairs (source, destination) block pairs (2 int64 each) that the
+ * caller must copy with pkv_copy_blocks before writing the new tokens;
+ * *out_n_pairs their number (0 or 1 here). PKV_ERR_OUT_OF_BLOCKS if the pool
+ * is too small; PKV_ERR_INVALID_ARG if max_pairs is too small. */
+int pkv_seq_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int64_t* out_slots,
+                   int64_t* out_cow_pairs, int32_t max_pairs, int32_t* out_n_pairs);
+/* Batched append: n_tokens[i] tokens to seq_ids[i] for i < n_seqs (no
+ * duplicates), in that order, all or nothing. Slots of all new tokens are
+ * written back to back to out_slots (sum of n_tokens entries). */
+int pkv_batch_append(pkv_allocator* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                     int32_t n_seqs, int64_t* out_slots, int64_t* out_cow_pairs,
+                     int32_t max_pairs, int32_t* out_n_pairs);
+/* Make child share every block of parent (refcount +1 each); child gets
+ * parent's length. Used for shared prefixes and parallel sampling. */
+int pkv_seq_fork(pkv_allocator* a, int64_t parent_id, int64_t child_id);
+/* Release a sequence (tail first, see above). */
+int pkv_seq_free(pkv_allocator* a, int64_t seq_id);
+/* Length of a sequence in tokens. */
+int pkv_seq_len(pkv_allocator* a, int64_t seq_id, int64_t* out);
+/* Dense block table for n sequences: table[n][max_blocks] (int32, row-major)
+ * with unused entries set to the null block 0, and context_lens[n] (int32,
+ * may be NULL). PKV_ERR_INVALID_ARG if a sequence needs more than max_blocks
+ * blocks. Host buffers (e.g. pinned, then copied to the device). */
+int pkv_fill_block_table(pkv_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* table,
+                         int32_t max_blocks, int32_t* context_lens);
+/* Refcount of one block (the null block reports 0). */
+int pkv_block_refcount(pkv_allocator* a, int32_t block, int32_t* out);
+/* Number of blocks in the free queue. */
+int pkv_num_free_blocks(pkv_allocator* a, int32_t* out);
+/* Pool accounting (see pkv_stats); utilisation is the share of in-use slots
+ * that hold token state ["vLLM: what PagedAttention turned into", section
+ * "Checking the 96.3%"]. */
+int pkv_allocator_stats(pkv_allocator* a, pkv_stats* out);
+/* How many blocks (null block included) fit in `bytes` of device memory for
+ * K and V pools of the given shape: floor(bytes / (2*num_kv_heads*16*head_dim
+ * *elem_size)). The engine sizes its pool once this way at start-up ["vLLM:
+ * what PagedAttention turned into", section "Checking the 96.3%"]. */
+int pkv_blocks_for_bytes(int64_t bytes, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         int32_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* Device kernels (asynchronous on `stream`). */
+
+/* Scatter new tokens into the pools through the slot mapping ["vLLM: what
+ * PagedAttention turned into", "The problem PagedAttention was actually
+ * solving"; "My Understanding of vLLM and PagedAttention", "Step 3 -- Tokens
+ * Generated Sequentially"]:
+ *   k_cache[slot/16][h][slot%16][:] = k_new[t][h][:]   (and V alike)
+ * for t < num_tokens. k_new/v_new: device [num_tokens][num_kv_heads][head_dim]
+ * with a stride of new_token_stride elements between tokens (>= num_kv_heads
+ * *head_dim; heads and dims contiguous). slot_mapping: device int64
+ * [num_tokens]. A slot < 0 or >= num_blocks*16 is skipped (no write). Two
+ * tokens with the same slot in one call race (caller error). Bit-exact copy. */
+int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          int64_t new_token_stride, const int64_t* slot_mapping,
+                          int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t dtype, void* stream);
+
+/* Copy whole blocks, K and V: for each pair i < n, block pairs[2i+1] becomes a
+ * copy of block pairs[2i] (copy-on-write of a shared block ["vLLM: what
+ * PagedAttention turned into", section "What a block hash actually is"]).
+ * pairs: device int64 [n][2]. Pairs with an id outside [0, num_blocks) are
+ * skipped. Destinations must be distinct and must not be sources of other
+ * pairs in the same call. */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    void* stream);
+
+/* Workspace bytes pkv_paged_attention_decode needs for these sizes on the
+ * current device (split-KV partial results and bookkeeping). The size does
+ * not depend on context lengths. */
+int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, size_t* out);
+
+/* Decode attention: one query token per sequence over its paged KV
+ * ["My Understanding of vLLM and PagedAttention", "3. PagedAttention CUDA
+ * Kernel" and "Step 4 -- Attention Computation"]:
+ *   out[s][h] = sum_{t < n_s} softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
+ * K_s/V_s = sequence s's tokens in logical order for KV head
+ * h / (num_q_heads/num_kv_heads); n_s = context_lens[s] counts every cached
+ * token including the current one (write it with pkv_reshape_and_cache first).
+ * n_s == 0 gives a zero output. n_s is clamped to [0, max_blocks_per_seq*16];
+ * block ids outside [0, num_blocks) read block 0 instead.
+ * q, out: device [num_seqs][num_q_heads][head_dim] in `dtype` (fp32
+ * accumulation, output rounded to nearest even for bf16). block_table: device
+ * int32 [num_seqs][max_blocks_per_seq]. context_lens: device int32 [num_seqs].
+ * workspace: device, >= pkv_decode_workspace_size(...) bytes, no
+ * initialisation needed; its contents are scratch.
+ * Long contexts are split across workgroups (split-KV) and the partial
+ * softmax states merged by a second kernel; the result does not depend on the
+ * physical placement of blocks. */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float scale, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pkv_paged_attention_prefill_chunk needs (0 if none). */
+int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                               int32_t max_context_len, size_t* out);
+
+/* Chunked-prefill attention: each chunk is a run of consecutive query tokens
+ * of one sequence, attending causally to the sequence's cached tokens plus
+ * the chunk's own ["(2) vLLM Internals ...", section "2. Continuous
+ * Batching"; "vLLM: what PagedAttention turned into", section "The
+ * scheduler, and what it has to balance now"]. Chunk c owns query rows
+ * cu_q_lens[c] .. cu_q_lens[c+1]-1 of q/out; context_lens[c] is the
+ * sequence's total length including the chunk (the chunk's K/V are already
+ * in the pool), so query i of the chunk sits at position
+ * p = context_lens[c] - q_len_c + i and attends to positions 0..p.
+ * q, out: device [cu_q_lens[num_chunks]][num_q_heads][head_dim] in `dtype`.
+ * cu_q_lens: device int32 [num_chunks+1], non-decreasing from 0.
+ * context_lens: device int32 [num_chunks]. block_table: device int32
+ * [num_chunks][max_blocks_per_seq]. max_q_len bounds every chunk's length
+ * (rows beyond it are not computed). Chunks with context_lens < q_len are
+ * treated as starting at position 0. */
+int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                      const int32_t* context_lens, const int32_t* block_table,
+                                      const void* k_cache, const void* v_cache,
+                                      int32_t num_chunks, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_q_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float scale, int32_t dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

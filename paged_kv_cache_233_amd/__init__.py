@@ -1,0 +1,359 @@
+"""Paged KV-cache attention for MI355X (gfx950).
+
+A thin ctypes binding of ``libpkv.so`` (built from ``csrc/``): argument
+marshalling only. Every step of the hot path runs in the library: the host
+block allocator in C++, and the scatter, block copy, decode and
+chunked-prefill attention in HIP kernels. PyTorch provides device memory and
+the stream; tensors are passed as raw pointers with
+``torch.cuda.current_stream()``.
+
+There is no fallback: if the library cannot be built or loaded, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["Error", "Allocator", "library", "reshape_and_cache", "copy_blocks",
+           "decode_workspace_size", "decode", "prefill_workspace_size", "prefill_chunk",
+           "F32", "BF16", "BLOCK_SIZE"]
+
+BLOCK_SIZE = 16
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_c_f = ctypes.c_float
+_c_sz = ctypes.c_size_t
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("used_blocks", ctypes.c_int32),
+                ("free_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("logical_tokens", ctypes.c_int64), ("stored_tokens", ctypes.c_int64),
+                ("utilisation", ctypes.c_double)]
+
+
+_SIGNATURES = {
+    "pkv_last_error": ([], ctypes.c_char_p),
+    "pkv_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "pkv_version": ([], ctypes.c_int),
+    "pkv_allocator_create": ([_c_i32, ctypes.POINTER(_c_p)], ctypes.c_int),
+    "pkv_allocator_destroy": ([_c_p], ctypes.c_int),
+    "pkv_allocator_set_free_order": ([_c_p, _c_p, _c_i32], ctypes.c_int),
+    "pkv_seq_add": ([_c_p, _c_i64], ctypes.c_int),
+    "pkv_seq_append": ([_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
+    "pkv_batch_append": ([_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
+    "pkv_seq_fork": ([_c_p, _c_i64, _c_i64], ctypes.c_int),
+    "pkv_seq_free": ([_c_p, _c_i64], ctypes.c_int),
+    "pkv_seq_len": ([_c_p, _c_i64, _c_p], ctypes.c_int),
+    "pkv_fill_block_table": ([_c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p], ctypes.c_int),
+    "pkv_block_refcount": ([_c_p, _c_i32, _c_p], ctypes.c_int),
+    "pkv_num_free_blocks": ([_c_p, _c_p], ctypes.c_int),
+    "pkv_allocator_stats": ([_c_p, ctypes.POINTER(Stats)], ctypes.c_int),
+    "pkv_blocks_for_bytes": ([_c_i64, _c_i32, _c_i32, _c_i32, _c_p], ctypes.c_int),
+    "pkv_reshape_and_cache": ([_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i32,
+                               _c_i32, _c_i32, _c_p], ctypes.c_int),
+    "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p],
+                        ctypes.c_int),
+    "pkv_decode_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)],
+                                  ctypes.c_int),
+    "pkv_paged_attention_decode": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
+                                   ctypes.c_int),
+    "pkv_prefill_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    ctypes.POINTER(_c_sz)], ctypes.c_int),
+    "pkv_paged_attention_prefill_chunk": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                           _c_i32, _c_p, _c_sz, _c_p], ctypes.c_int),
+}
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpkv.so (built in place first if it is missing)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                from . import build as _build
+                _build.build()
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = lib
+        return _lib
+
+
+class Error(RuntimeError):
+    """A negative status from libpkv; ``code`` is the PKV_ERR_* value."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__("%s (%d): %s" % (library().pkv_strerror(code).decode(), code, message))
+        self.code = code
+        self.message = message
+
+
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_OUT_OF_BLOCKS = -3
+ERR_NO_SUCH_SEQ = -4
+ERR_SEQ_EXISTS = -5
+ERR_WORKSPACE = -6
+ERR_HIP = -7
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise Error(code, library().pkv_last_error().decode())
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# --------------------------------------------------------------- allocator
+class Allocator:
+    """Host block allocator (C++): null block 0, LIFO reuse, tail-first
+    release, refcounted sharing with copy-on-write."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = library()
+        h = _c_p()
+        _check(self._lib.pkv_allocator_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_free_order(self, order) -> None:
+        o = np.ascontiguousarray(order, dtype=np.int32)
+        _check(self._lib.pkv_allocator_set_free_order(self._h, _ptr(o), int(o.size)))
+
+    def add(self, sid: int) -> None:
+        _check(self._lib.pkv_seq_add(self._h, int(sid)))
+
+    def append(self, sid: int, n: int, max_pairs: int = 1) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        return self.batch_append([sid], [n], max_pairs)
+
+    def batch_append(self, sids: Sequence[int], ns: Sequence[int], max_pairs: Optional[int] = None
+                     ) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        """Append ns[i] tokens to sids[i]; returns (int64 slots, copy pairs)."""
+        s = np.ascontiguousarray(sids, dtype=np.int64)
+        n = np.ascontiguousarray(ns, dtype=np.int32)
+        slots = np.empty(int(n.sum()), dtype=np.int64)
+        mp = len(s) if max_pairs is None else int(max_pairs)
+        pairs = np.empty(max(1, 2 * mp), dtype=np.int64)
+        npairs = _c_i32(0)
+        _check(self._lib.pkv_batch_append(self._h, _ptr(s), _ptr(n), int(s.size), _ptr(slots),
+                                          _ptr(pairs), mp, ctypes.byref(npairs)))
+        k = npairs.value
+        return slots, [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(k)]
+
+    def batch_append_into(self, sids: np.ndarray, ns: np.ndarray, slots_ptr: int,
+                          pairs: np.ndarray) -> int:
+        """Like batch_append, writing slots to raw host memory at slots_ptr
+        (e.g. a pinned tensor) and copy pairs to ``pairs`` (int64 [2*k]);
+        returns the number of pairs."""
+        npairs = _c_i32(0)
+        _check(self._lib.pkv_batch_append(self._h, _ptr(sids), _ptr(ns), int(sids.size), slots_ptr,
+                                          _ptr(pairs), int(pairs.size // 2), ctypes.byref(npairs)))
+        return npairs.value
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pkv_seq_fork(self._h, int(parent), int(child)))
+
+    def free(self, sid: int) -> None:
+        _check(self._lib.pkv_seq_free(self._h, int(sid)))
+
+    def seq_len(self, sid: int) -> int:
+        out = _c_i64(0)
+        _check(self._lib.pkv_seq_len(self._h, int(sid), ctypes.byref(out)))
+        return out.value
+
+    def block_table(self, sids: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(sids, dtype=np.int64)
+        table = np.empty((s.size, int(max_blocks)), dtype=np.int32)
+        lens = np.empty(s.size, dtype=np.int32)
+        _check(self._lib.pkv_fill_block_table(self._h, _ptr(s), int(s.size), _ptr(table),
+                                              int(max_blocks), _ptr(lens)))
+        return table, lens
+
+    def fill_block_table_into(self, sids: np.ndarray, table_ptr: int, max_blocks: int,
+                              lens_ptr: int) -> None:
+        """Write the table and lengths to raw host memory (e.g. pinned tensors)."""
+        _check(self._lib.pkv_fill_block_table(self._h, _ptr(sids), int(sids.size), table_ptr,
+                                              int(max_blocks), lens_ptr))
+
+    def refcount(self, block: int) -> int:
+        out = _c_i32(0)
+        _check(self._lib.pkv_block_refcount(self._h, int(block), ctypes.byref(out)))
+        return out.value
+
+    def num_free(self) -> int:
+        out = _c_i32(0)
+        _check(self._lib.pkv_num_free_blocks(self._h, ctypes.byref(out)))
+        return out.value
+
+    def stats(self) -> Dict[str, float]:
+        st = Stats()
+        _check(self._lib.pkv_allocator_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in Stats._fields_}
+
+
+def blocks_for_bytes(nbytes: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:
+    out = _c_i32(0)
+    _check(library().pkv_blocks_for_bytes(int(nbytes), int(num_kv_heads), int(head_dim), int(dtype),
+                                          ctypes.byref(out)))
+    return out.value
+
+
+# ------------------------------------------------------------------ kernels
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise Error(ERR_UNSUPPORTED, "tensor dtype %s not supported" % t.dtype)
+
+
+def _dev(t, name: str, dtype=None):
+    if not t.is_cuda:
+        raise Error(ERR_INVALID_ARG, "%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise Error(ERR_INVALID_ARG, "%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise Error(ERR_INVALID_ARG, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _pool_shape(k_cache):
+    if k_cache.dim() != 4 or k_cache.shape[2] != BLOCK_SIZE:
+        raise Error(ERR_INVALID_ARG, "pool must be [num_blocks, num_kv_heads, 16, head_dim]")
+    nb, hkv, _, d = k_cache.shape
+    return int(nb), int(hkv), int(d)
+
+
+def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+    """Scatter k_new/v_new [T, Hkv, D] into the pools at slot_mapping (int64 [T])."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "k_cache and v_cache differ")
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (hkv, d) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise Error(ERR_INVALID_ARG, "k_new/v_new must be [T, %d, %d]" % (hkv, d))
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    t = int(k_new.shape[0])
+    if slot_mapping.numel() != t:
+        raise Error(ERR_INVALID_ARG, "slot_mapping must hold %d entries" % t)
+    _check(library().pkv_reshape_and_cache(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), hkv * d, _dev(slot_mapping, "slot_mapping", torch.int64), t, nb, hkv, d,
+        _dtype_code(k_cache), _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """For each row (src, dst) of pairs (int64 [n, 2]), copy block src to dst."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    n = int(pairs.numel() // 2)
+    _check(library().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                     _dev(pairs, "pairs", torch.int64), n, nb, hkv, d,
+                                     _dtype_code(k_cache), _stream(stream)))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    out = _c_sz(0)
+    _check(library().pkv_decode_workspace_size(int(num_seqs), int(num_q_heads), int(num_kv_heads),
+                                               int(head_dim), ctypes.byref(out)))
+    return out.value
+
+
+def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, workspace,
+           stream=None) -> None:
+    """Paged decode attention; q/out [S, Hq, D], block_table int32 [S, maxB],
+    context_lens int32 [S], workspace a uint8 device tensor of at least
+    decode_workspace_size(...) bytes."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
+        raise Error(ERR_INVALID_ARG, "q/out must be [S, Hq, %d]" % d)
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    s, hq = int(q.shape[0]), int(q.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != s or context_lens.numel() != s:
+        raise Error(ERR_INVALID_ARG, "block_table must be [S, maxB] and context_lens [S]")
+    _check(library().pkv_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def prefill_workspace_size(num_chunks: int, total_q: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_q_len: int, max_context_len: int) -> int:
+    out = _c_sz(0)
+    _check(library().pkv_prefill_workspace_size(int(num_chunks), int(total_q), int(num_q_heads),
+                                                int(num_kv_heads), int(head_dim), int(max_q_len),
+                                                int(max_context_len), ctypes.byref(out)))
+    return out.value
+
+
+def prefill_chunk(out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache, max_q_len: int,
+                  scale: float, workspace=None, stream=None) -> None:
+    """Causal chunked-prefill attention; q/out [Tq, Hq, D], cu_q_lens int32
+    [C+1], context_lens int32 [C] (including the chunk), block_table int32
+    [C, maxB]."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
+        raise Error(ERR_INVALID_ARG, "q/out must be [Tq, Hq, %d]" % d)
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    c = int(context_lens.numel())
+    if cu_q_lens.numel() != c + 1 or block_table.dim() != 2 or block_table.shape[0] != c:
+        raise Error(ERR_INVALID_ARG, "cu_q_lens [C+1], context_lens [C], block_table [C, maxB]")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    _check(library().pkv_paged_attention_prefill_chunk(
+        _dev(out, "out"), _dev(q, "q"), _dev(cu_q_lens, "cu_q_lens", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), c, nb, int(block_table.shape[1]),
+        int(max_q_len), int(q.shape[1]), hkv, d, float(scale), _dtype_code(q), ws_ptr, ws_bytes,
+        _stream(stream)))

@@ -1,0 +1,197 @@
+// C entry points of the device kernels: argument checks on the host, then an
+// asynchronous launch on the caller's stream. Also the error-message plumbing.
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace pkv {
+
+namespace {
+thread_local char g_msg[512] = "";
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+
+int check_shape(int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+  return PKV_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
+                num_q_heads / num_kv_heads);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return pkv::g_msg; }
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_OUT_OF_BLOCKS: return "out of KV blocks";
+    case PKV_ERR_NO_SUCH_SEQ: return "no such sequence";
+    case PKV_ERR_SEQ_EXISTS: return "sequence exists";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          int64_t new_token_stride, const int64_t* slot_mapping,
+                          int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t dtype, void* stream) {
+  pkv::clear_error();
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (num_tokens < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (new_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PKV_ERR_INVALID_ARG, "new_token_stride %lld < num_kv_heads*head_dim",
+                (long long)new_token_stride);
+  if (num_tokens > INT32_MAX / 2) return fail(PKV_ERR_INVALID_ARG, "too many tokens");
+  const int64_t elem = dtype == PKV_F32 ? 4 : 2;
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) % 16 != 0 ||
+      (new_token_stride * elem) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pools, new K/V and the token stride must be 16-byte aligned");
+  hipError_t err = pkv::launch_reshape_and_cache(k_cache, v_cache, k_new, v_new, new_token_stride,
+                                                 slot_mapping, num_tokens, num_blocks, num_kv_heads,
+                                                 head_dim, dtype, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "reshape_and_cache launch");
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    void* stream) {
+  pkv::clear_error();
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (n < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  hipError_t err = pkv::launch_copy_blocks(k_cache, v_cache, pairs, n, num_blocks, num_kv_heads,
+                                           head_dim, dtype, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "copy_blocks launch");
+}
+
+int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, size_t* out) {
+  pkv::clear_error();
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs < 0");
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
+  *out = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  return PKV_OK;
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float scale, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  pkv::clear_error();
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (num_seqs < 0 || num_blocks <= 0 || max_blocks_per_seq < 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 1) > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs*num_kv_heads*max_blocks_per_seq too large");
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache |
+       (uintptr_t)workspace) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "q, out, pools and workspace must be 16-byte aligned");
+  if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
+  size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                    max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                    workspace};
+  hipError_t err = pkv::launch_decode(a, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
+}
+
+int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
+                               int32_t max_context_len, size_t* out) {
+  pkv::clear_error();
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  if (num_chunks < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  *out = 0;
+  return PKV_OK;
+}
+
+int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                      const int32_t* context_lens, const int32_t* block_table,
+                                      const void* k_cache, const void* v_cache,
+                                      int32_t num_chunks, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_q_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  pkv::clear_error();
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (num_chunks < 0 || num_blocks <= 0 || max_blocks_per_seq < 0 || max_q_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_chunks == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !cu_q_lens || !context_lens || !k_cache || !v_cache ||
+      (!block_table && max_blocks_per_seq > 0))
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((int64_t)num_chunks * num_kv_heads * ((max_q_len + 15) / 16) > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "grid too large");
+  pkv::PrefillArgs a{out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache, num_chunks,
+                     num_blocks, max_blocks_per_seq, max_q_len, num_q_heads, num_kv_heads,
+                     head_dim, scale, dtype};
+  hipError_t err = pkv::launch_prefill(a, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "prefill launch");
+}
+
+}  // extern "C"

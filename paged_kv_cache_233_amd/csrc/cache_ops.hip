@@ -1,0 +1,93 @@
+// Writes into the paged KV pools: the slot-mapped scatter of new tokens and
+// whole-block copies for copy-on-write.
+//
+// Pool layout [num_blocks][num_kv_heads][16][head_dim]; slot = block*16 +
+// offset ("vLLM: what PagedAttention turned into", section "The problem
+// PagedAttention was actually solving", on the int64 slot mapping the worker
+// keeps per scheduled token). Both kernels move 16-byte vectors: one token's
+// row for one head is head_dim*elem bytes (128, 256 or 512), so every thread
+// reads and writes aligned 16-byte pieces and a wave covers 1 KiB of
+// consecutive bytes on both sides.
+#include "internal.h"
+
+namespace {
+
+// One thread per (token, tensor, head, 16-byte piece). `pieces` is the
+// number of 16-byte pieces in one head row.
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                         const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                         int64_t token_stride_vec, const int64_t* __restrict__ slots,
+                         int64_t num_tokens, int64_t num_slots, int32_t num_kv_heads,
+                         int32_t pieces) {
+  const int64_t per_tensor = (int64_t)num_kv_heads * pieces;
+  const int64_t per_token = 2 * per_tensor;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= num_tokens * per_token) return;
+  const int64_t t = idx / per_token;
+  int64_t r = idx - t * per_token;
+  const bool is_v = r >= per_tensor;
+  if (is_v) r -= per_tensor;
+  const int32_t h = (int32_t)(r / pieces);
+  const int32_t piece = (int32_t)(r - (int64_t)h * pieces);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding or out-of-range: no write
+  const int64_t blk = slot >> 4;
+  const int64_t off = slot & 15;
+  const uint4* src = (is_v ? v_new : k_new) + t * token_stride_vec + (int64_t)h * pieces + piece;
+  uint4* dst = (is_v ? v_cache : k_cache) +
+               ((blk * num_kv_heads + h) * 16 + off) * pieces + piece;
+  *dst = *src;
+}
+
+// One workgroup per copy pair; the block's K and V bytes are copied in
+// 16-byte pieces.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                   const int64_t* __restrict__ pairs, int32_t num_blocks, int32_t block_vecs) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* ks = k_cache + src * block_vecs;
+  const uint4* vs = v_cache + src * block_vecs;
+  uint4* kd = k_cache + dst * block_vecs;
+  uint4* vd = v_cache + dst * block_vecs;
+  for (int32_t i = threadIdx.x; i < block_vecs; i += blockDim.x) {
+    uint4 a = ks[i];
+    uint4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+}  // namespace
+
+namespace pkv {
+
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,
+                                    const void* v_new, int64_t token_stride,
+                                    const int64_t* slots, int64_t num_tokens, int32_t num_blocks,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    hipStream_t stream) {
+  const int elem = dtype == PKV_F32 ? 4 : 2;
+  const int32_t pieces = head_dim * elem / 16;
+  const int64_t total = num_tokens * 2 * num_kv_heads * pieces;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (uint4*)k_cache, (uint4*)v_cache, (const uint4*)k_new, (const uint4*)v_new,
+                     token_stride * elem / 16, slots, num_tokens, (int64_t)num_blocks * 16,
+                     num_kv_heads, pieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t dtype, hipStream_t stream) {
+  const int elem = dtype == PKV_F32 ? 4 : 2;
+  const int32_t block_vecs = num_kv_heads * 16 * head_dim * elem / 16;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, stream, (uint4*)k_cache,
+                     (uint4*)v_cache, pairs, num_blocks, block_vecs);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

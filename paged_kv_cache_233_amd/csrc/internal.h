@@ -1,0 +1,82 @@
+// Internal declarations shared by the host-side translation units of libpkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <string>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Records a message for pkv_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the per-thread message.
+void clear_error();
+// Maps a HIP error from a launch to PKV_ERR_HIP with a message.
+int hip_fail(hipError_t e, const char* what);
+
+constexpr int kBlock = PKV_BLOCK_SIZE;
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments were validated by
+// the caller.
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,
+                                    const void* v_new, int64_t token_stride,
+                                    const int64_t* slots, int64_t num_tokens, int32_t num_blocks,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t dtype, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+  int32_t dtype;
+  void* workspace;
+};
+
+// Number of waves the split-KV decode kernel is launched with on the current
+// device (a multiple of 8), and the workspace it needs.
+int decode_num_waves();
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const int32_t* cu_q_lens;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_chunks;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_q_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float scale;
+  int32_t dtype;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv
