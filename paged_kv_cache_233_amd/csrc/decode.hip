@@ -461,16 +461,24 @@ decode_merge_kernel(DecodeParams p) {
   const int32_t w1 = (int32_t)(((last + 1) * W + total - 1) / total - 1);
   if (w0 == w1) return;  // written directly by its wave
   const int32_t stride = G * (D + 4);
+  // Waves w0..w1 overlap the sequence; those with an empty range (possible
+  // when there are fewer tiles than waves) wrote nothing and are skipped.
+  // A wave whose range starts before the sequence holds it in its second
+  // slot, every other one in its first.
   for (int32_t e = lane; e < G * D; e += 64) {
     const int32_t h = e / D;
     float mmax = -INFINITY;
     for (int32_t w = w0; w <= w1; ++w) {
-      const int32_t slot = 2 * w + ((total * w / W) < first ? 1 : 0);
+      const int64_t st = total * w / W;
+      if (st == total * (w + 1) / W) continue;
+      const int32_t slot = 2 * w + (st < first ? 1 : 0);
       mmax = fmaxf(mmax, p.ws_partial[(int64_t)slot * stride + G * D + h]);
     }
     float num = 0.f, den = 0.f;
     for (int32_t w = w0; w <= w1; ++w) {
-      const int32_t slot = 2 * w + ((total * w / W) < first ? 1 : 0);
+      const int64_t st = total * w / W;
+      if (st == total * (w + 1) / W) continue;
+      const int32_t slot = 2 * w + (st < first ? 1 : 0);
       const float* base = p.ws_partial + (int64_t)slot * stride;
       const float sc = __builtin_amdgcn_exp2f(base[G * D + h] - mmax);
       num += sc * base[e];

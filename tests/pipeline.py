@@ -75,9 +75,7 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
     vc = torch.full(shape, float("nan"), dtype=dt, device=device)
     kv = KVCache(w)
     script = _positions(w)
-    last_use = {}
-    for i, (sid, _, _) in enumerate(script):
-        last_use[sid] = i
+    res_pairs = []
     j = 0
     for op in w.setup_ops():
         if op[0] == "add":
@@ -87,7 +85,9 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
         else:
             sid, p0, n = script[j]
             slots, pairs = a.append(sid, n)
-            assert pairs == []
+            if pairs:   # copy-on-write of a shared, partially filled last block
+                pkv.copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device=device))
+                res_pairs.extend(pairs)
             k, v = kv.get(sid)
             pkv.reshape_and_cache(kc, vc, k[p0:p0 + n].to(device), v[p0:p0 + n].to(device),
                                   torch.from_numpy(slots).to(device))
@@ -95,7 +95,9 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
     # the step: new tokens of every sequence, one batched append and scatter
     ids, ns = w.step_appends()
     slots, pairs = a.batch_append(ids, ns)
-    assert pairs == []
+    if pairs:
+        pkv.copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device=device))
+        res_pairs.extend(pairs)
     ks, vs = [], []
     for sid, n in zip(ids, ns):
         k, v = kv.get(sid)
@@ -105,7 +107,7 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
     if ids:
         pkv.reshape_and_cache(kc, vc, torch.cat(ks).to(device), torch.cat(vs).to(device),
                               torch.from_numpy(slots).to(device))
-    res = {"step_slots": slots}
+    res = {"step_slots": slots, "cow_pairs": res_pairs}
     dec = w.decode_seqs
     maxb = w.max_blocks_per_seq()
     if dec:
@@ -161,6 +163,7 @@ def run_oracle(w: workloads.Workload, decode_sample: Optional[Sequence[int]] = N
     vp = paged.new_pool(w.num_blocks, w.num_kv_heads, w.head_dim, storage)
     kv = KVCache(w)
     script = _positions(w)
+    res_pairs = []
     j = 0
     for op in w.setup_ops():
         if op[0] == "add":
@@ -169,14 +172,20 @@ def run_oracle(w: workloads.Workload, decode_sample: Optional[Sequence[int]] = N
             m.fork(op[1], op[2])
         else:
             sid, p0, n = script[j]
-            slots, _ = m.append(sid, n)
+            slots, pairs = m.append(sid, n)
+            paged.copy_blocks(kp, pairs)
+            paged.copy_blocks(vp, pairs)
+            res_pairs.extend(pairs)
             if sid in keep:
                 k, v = kv.get(sid)
                 paged.scatter(kp, to_numpy_storage(k[p0:p0 + n]), slots)
                 paged.scatter(vp, to_numpy_storage(v[p0:p0 + n]), slots)
             j += 1
     ids, ns = w.step_appends()
-    slots, _ = m.batch_append(ids, ns)
+    slots, pairs = m.batch_append(ids, ns)
+    paged.copy_blocks(kp, pairs)
+    paged.copy_blocks(vp, pairs)
+    res_pairs.extend(pairs)
     off = 0
     for sid, n in zip(ids, ns):
         if sid in keep:
@@ -186,7 +195,7 @@ def run_oracle(w: workloads.Workload, decode_sample: Optional[Sequence[int]] = N
             paged.scatter(vp, to_numpy_storage(v[spec.cached:spec.total]), slots[off:off + n])
         off += n
     res = {"step_slots": np.array(slots, dtype=np.int64), "k_cache": kp, "v_cache": vp,
-           "model": m}
+           "model": m, "cow_pairs": res_pairs}
     maxb = w.max_blocks_per_seq()
     if dec:
         idx = list(range(len(dec))) if decode_sample is None else list(decode_sample)

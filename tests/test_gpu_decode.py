@@ -104,7 +104,7 @@ SMALL = {
     "shared prefix": lambda: workloads.custom(
         "shared", 27, [100, 120, 140, 161, 200], shared_prefix=96, num_q_heads=32, num_kv_heads=8,
         head_dim=128, dtype="bf16"),
-    "shared prefix partial block": lambda: workloads.custom(
+    "shared prefix partial block (copy-on-write)": lambda: workloads.custom(
         "shared2", 28, [40, 50, 60], shared_prefix=37, num_q_heads=8, num_kv_heads=2,
         head_dim=64, dtype="f32"),
     "llama/16": lambda: workloads.scaled("llama", 16),
@@ -114,6 +114,7 @@ SMALL = {
 
 
 def _check_tables(nat, ora):
+    assert nat["cow_pairs"] == ora["cow_pairs"]
     assert np.array_equal(nat["step_slots"], ora["step_slots"])
     assert np.array_equal(nat["decode_table"], ora["decode_table"])
     assert np.array_equal(nat["decode_lens"], ora["decode_lens"])
