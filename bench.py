@@ -1,0 +1,289 @@
+"""Benchmark of the paged KV-cache decode hot path on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch:
+  host   append one token to every sequence (C++ allocator), fill the block
+         table and context lengths into pinned buffers, copy them and the
+         slot mapping to the device (asynchronous);
+  device reshape_and_cache of the new tokens' K/V, then paged decode
+         attention (one split-KV kernel; split sequences are merged by the
+         last wave that finishes them).
+Consecutive steps cycle through R copies of the KV pool, as consecutive
+layers of a model would, so every step reads its keys and values from HBM
+and not from the 256 MB last-level cache. Inputs are resident in HBM before
+timing starts.
+
+Workload (default): 64 sequences, context lengths uniform in [128, 4096],
+32 query / 8 KV heads, head_dim 128, bf16, blocks of 16 tokens placed at
+random in a pool of 1.5x the need (block 0 = null block).
+
+Prints one JSON line (metric: KV-read GB/s over the whole step; decode
+tokens/s beside it), with a roofline object for the decode kernels and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: KV-read HBM GB/s (% of peak) + tokens/s, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama", choices=["llama", "long", "shared", "mixed"])
+    ap.add_argument("--pools", type=int, default=4, help="KV pool copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=64)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per decode launch from the committed counter runs, if they
+    were taken on the current decode source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (this build has no multi-GPU path); "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.named(args.config)
+    dec = w.decode_seqs
+    S = len(dec)
+    extra = args.warmup + args.steps + 2
+    nb = w.num_blocks + S * (extra // 16 + 2)
+    maxb = w.max_blocks_per_seq(extra)
+    dt = w.torch_dtype
+    log("workload %s: %d decode seqs, pool %d blocks, max %d blocks/seq" % (w.name, S, nb, maxb))
+
+    # ---------------------------------------------------------------- setup
+    alloc = pkv.Allocator(nb)
+    order = np.concatenate([w.free_order, np.arange(w.num_blocks, nb, dtype=np.int32)])
+    alloc.set_free_order(order)
+    shape = (nb, w.num_kv_heads, 16, w.head_dim)
+    kc0 = torch.zeros(shape, dtype=dt, device=dev)
+    vc0 = torch.zeros(shape, dtype=dt, device=dev)
+    specs = {s.seq_id: s for s in w.seqs}
+    cur = {}
+    kvcache = {}
+    for op in w.setup_ops():
+        if op[0] == "add":
+            alloc.add(op[1])
+            cur[op[1]] = 0
+        elif op[0] == "fork":
+            alloc.fork(op[1], op[2])
+            cur[op[2]] = cur[op[1]]
+        else:
+            sid, n = op[1], op[2]
+            slots, pairs = alloc.append(sid, n)
+            if pairs:
+                pkv.copy_blocks(kc0, vc0, torch.tensor(pairs, dtype=torch.int64, device=dev))
+            if sid not in kvcache:
+                kvcache[sid] = w.seq_kv(specs[sid])
+            k, v = kvcache[sid]
+            p0 = cur[sid]
+            pkv.reshape_and_cache(kc0, vc0, k[p0:p0 + n].to(dev), v[p0:p0 + n].to(dev),
+                                  torch.from_numpy(slots).to(dev))
+            cur[sid] = p0 + n
+    kvcache.clear()
+    torch.cuda.synchronize()
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.pools - 1)]
+    sids = np.array([s.seq_id for s in dec], dtype=np.int64)
+    ones = np.ones(S, dtype=np.int32)
+    gen = torch.Generator().manual_seed(1234)
+    q = torch.randn((S, w.num_q_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    k_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    v_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
+    # double-buffered pinned host staging for the per-step host->device copy
+    pin_slots = [torch.empty(S, dtype=torch.int64).pin_memory() for _ in range(2)]
+    pin_table = [torch.empty((S, maxb), dtype=torch.int32).pin_memory() for _ in range(2)]
+    pin_lens = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    d_slots = torch.empty(S, dtype=torch.int64, device=dev)
+    d_table = torch.empty((S, maxb), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+    pairs_buf = np.empty(2 * S, dtype=np.int64)
+    kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    stream = torch.cuda.current_stream()
+
+    total_steps = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
+    ctx_tokens = []
+
+    def step(t):
+        b = t % 2
+        if t >= 2:
+            copied[b].synchronize()      # the copy that last read this staging buffer is done
+        npairs = alloc.batch_append_into(sids, ones, pin_slots[b].data_ptr(), pairs_buf)
+        assert npairs == 0
+        alloc.fill_block_table_into(sids, pin_table[b].data_ptr(), maxb, pin_lens[b].data_ptr())
+        ctx_tokens.append(int(pin_lens[b].numpy().sum()))
+        d_slots.copy_(pin_slots[b], non_blocking=True)
+        d_table.copy_(pin_table[b], non_blocking=True)
+        d_lens.copy_(pin_lens[b], non_blocking=True)
+        copied[b].record(stream)
+        kc, vc = pools[t % len(pools)]
+        e0, e1, e2 = ev[t]
+        e0.record(stream)
+        pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots)
+        e1.record(stream)
+        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws)
+        e2.record(stream)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total_steps):
+        step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    timed = range(args.warmup, total_steps)
+    rc_us = np.array([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in timed])
+    dec_us = np.array([ev[t][1].elapsed_time(ev[t][2]) * 1e3 for t in timed])
+    kv_bytes = np.array([ctx_tokens[t] * kv_bytes_per_token for t in timed], dtype=np.float64)
+    achieved = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
+    value = float(kv_bytes.sum() / wall / 1e9)
+    tokens_per_s = S * args.steps / wall
+    log("decode kernels: mean %.1f us (min %.1f, median %.1f); reshape_and_cache %.1f us; "
+        "step %.1f us wall" % (dec_us.mean(), dec_us.min(), np.median(dec_us), rc_us.mean(),
+                               ms_per_step * 1e3))
+
+    # ------------------------------------------------------- CPU oracle leg
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_sample_seqs)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s decode: %d seqs, ctx U[128,4096] (seeded), %d q / %d kv heads, "
+                               "head_dim %d, 16-token blocks, random placement, 1.5x pool"
+                               % (w.name, S, w.num_q_heads, w.num_kv_heads, w.head_dim)
+                   if w.name == "llama" else w.name,
+                   "num_seqs": S, "mean_context_tokens": round(float(kv_bytes.mean() / kv_bytes_per_token / S), 1),
+                   "kv_bytes_per_step": int(kv_bytes.mean()), "pool_copies_cycled": len(pools),
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(tokens_per_s, 1),
+        "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
+                      "decode_median": round(float(np.median(dec_us)), 2),
+                      "reshape_and_cache_mean": round(float(rc_us.mean()), 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(),
+                     "kernel": "paged_attention_decode (decode_split_kernel)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, nseq):
+    """The CPU oracle (NumPy float64), timed on host cores over a bounded
+    sample of the workload: the first ``nseq`` decode sequences. The oracle's
+    own allocator model and scatter build its pool and tables first (not
+    timed); the timed part is its decode attention (materialise through the
+    block table + float64 softmax attention)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import tests.pipeline as pl
+    from oracle import paged
+
+    dec = w.decode_seqs
+    sample = list(range(min(nseq, len(dec))))
+    t_setup = time.perf_counter()
+    with threadpool_limits(limits=1):
+        ora = pl.run_oracle(w, decode_sample=sample, prefill=False)
+        table = ora["decode_table"][sample]
+        lens = ora["decode_lens"][sample]
+        q = np.concatenate([pl.to_numpy_storage(w.seq_q(dec[i])) for i in sample])
+        log("oracle setup %.1f s" % (time.perf_counter() - t_setup))
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            paged.decode(q, ora["k_cache"], ora["v_cache"], table, lens, w.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 10.0 or reps >= 20:
+                break
+    tokens = int(lens.sum())
+    kv = float(tokens) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    gbs = kv * reps / el / 1e9
+    log("oracle: %d reps over %d seqs in %.2f s -> %.3f GB/s" % (reps, len(sample), el, gbs))
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d decode sequences of the same workload (%d context tokens), "
+                      "materialise + float64 softmax attention, %d repetitions, BLAS limited to "
+                      "1 thread" % (len(sample), len(dec), tokens, reps),
+            "seconds": round(el, 2), "tokens_per_s": round(len(sample) * reps / el, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -198,10 +198,11 @@ int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num
  * accumulation, output rounded to nearest even for bf16). block_table: device
  * int32 [num_seqs][max_blocks_per_seq]. context_lens: device int32 [num_seqs].
  * workspace: device, >= pkv_decode_workspace_size(...) bytes, no
- * initialisation needed; its contents are scratch.
- * Long contexts are split across workgroups (split-KV) and the partial
- * softmax states merged by a second kernel; the result does not depend on the
- * physical placement of blocks. */
+ * initialisation needed; its contents are scratch. Calls that overlap in
+ * time must not share a workspace.
+ * Long contexts are split across waves (split-KV) and the partial softmax
+ * states merged in token order by a second kernel, so the result is
+ * deterministic and does not depend on the physical placement of blocks. */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,

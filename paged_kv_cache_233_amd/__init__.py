@@ -20,7 +20,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Error", "Allocator", "library", "reshape_and_cache", "copy_blocks",
-           "decode_workspace_size", "decode", "prefill_workspace_size", "prefill_chunk",
+           "decode_workspace_size", "decode_workspace", "decode", "prefill_workspace_size", "prefill_chunk",
            "F32", "BF16", "BLOCK_SIZE"]
 
 BLOCK_SIZE = 16
@@ -305,11 +305,19 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
     return out.value
 
 
+def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     device="cuda"):
+    """A decode workspace (uint8 device tensor) of the size the library asks for."""
+    torch = _torch()
+    return torch.empty(decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim),
+                       dtype=torch.uint8, device=device)
+
+
 def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, workspace,
            stream=None) -> None:
     """Paged decode attention; q/out [S, Hq, D], block_table int32 [S, maxB],
     context_lens int32 [S], workspace a uint8 device tensor of at least
-    decode_workspace_size(...) bytes."""
+    decode_workspace_size(...) bytes (``decode_workspace`` allocates one)."""
     torch = _torch()
     nb, hkv, d = _pool_shape(k_cache)
     if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):

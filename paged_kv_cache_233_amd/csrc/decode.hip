@@ -17,8 +17,11 @@
 // A wave's range splits into pieces, one per (g, s) it touches. A piece that
 // covers a whole sequence writes the final output; any other piece writes
 // its partial softmax state (running max, sum, unnormalised output) to one of
-// the wave's two workspace slots, and a second kernel merges the partial
-// states of each split sequence in token order (deterministic, no atomics).
+// the wave's two workspace slots. A second kernel merges the partial states
+// of each split sequence in wave order, which is token order: the result is
+// deterministic and needs no atomics. (Merging in the last-arriving wave
+// instead would need a device-scope release per partial state, which writes
+// back the whole L2 of an XCD and costs far more than the second launch.)
 //
 // Per 16-token block and KV head the wave loads the K tile and the V tile
 // ([16][head_dim] each, contiguous) straight into registers and runs:
@@ -47,6 +50,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;        // workgroups are dealt round-robin over 8 XCDs
+constexpr int kIds = 1024;      // block ids staged in LDS per sub-piece
 
 template <int DT, int D>
 struct Shape {
@@ -56,7 +60,6 @@ struct Shape {
   static constexpr int kVWords = kRow / 64;    // 32-bit V words per lane per row
   static constexpr int kTiles = D / 16;        // 16-row MFMA tiles of head_dim
   static constexpr int kTileBytes = 16 * kRow; // one (block, head) tile
-  static constexpr int kDepth = kRow <= 256 ? 4 : 2;  // K/V tiles in flight per wave
 };
 
 template <int DT, int D>
@@ -94,14 +97,23 @@ __device__ __forceinline__ void load_tile(Tile<DT, D>& tl, const char* kb, const
   for (int j = 0; j < 4; ++j) load_words<Sh::kVWords>(tl.v[j], vb + v_off + j * Sh::kRow);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four token groups
+// of one head). The gfx950 row-swap instructions hand each lane the value of
+// its partner 16 (then 32) lanes away in a VALU operation, so the loop has no
+// LDS traffic and no LDS wait. The combine is commutative, so all four lanes
+// end with the same bits.
 __device__ __forceinline__ float wave_max_kg(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum_kg(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float bf16_round(float x) {
@@ -216,12 +228,18 @@ struct DecodeParams {
   float scale_log2;
 };
 
-// Blocks of sequence s after clamping its length to the table width.
+// Length of sequence s after clamping to [0, table width in tokens]; s may
+// differ per lane.
 __device__ __forceinline__ int32_t seq_len_clamped(const DecodeParams& p, int32_t s) {
   int32_t n = p.context_lens[s];
   n = n < 0 ? 0 : n;
   const int32_t cap = p.max_blocks * 16;
   return n > cap ? cap : n;
+}
+
+// The same for a wave-uniform s, kept in a scalar register.
+__device__ __forceinline__ int32_t seq_len_uniform(const DecodeParams& p, int32_t s) {
+  return __builtin_amdgcn_readfirstlane(seq_len_clamped(p, s));
 }
 
 // Inclusive prefix sum across the wave.
@@ -288,10 +306,104 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, const State
   }
 }
 
+// Logical wave whose tile range holds flat tile i: the largest w with
+// floor(w*total/W) <= i.
+__device__ __forceinline__ int32_t wave_of(int64_t i, int64_t total, int32_t W) {
+  return (int32_t)(((i + 1) * W + total - 1) / total - 1);
+}
+
+__device__ __forceinline__ bool wave_empty(int32_t w, int64_t total, int32_t W) {
+  return total * w / W == total * (w + 1) / W;
+}
+
+// Zero output of an empty sequence (all query heads).
 template <int DT, int D>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__device__ __forceinline__ void zero_rows(const DecodeParams& p, int32_t s) {
+  const int64_t elems = (int64_t)p.num_q_heads * D;
+  const int per = 16 / Shape<DT, D>::kElem;
+  char* row = reinterpret_cast<char*>(p.out) + (int64_t)s * elems * Shape<DT, D>::kElem;
+  for (int64_t e = (int64_t)threadIdx.x * per; e < elems; e += 64 * per)
+    *reinterpret_cast<uint4*>(row + e * Shape<DT, D>::kElem) = uint4{0u, 0u, 0u, 0u};
+}
+
+// Fold the partial states of sequence s, KV head g (flat tiles first..last)
+// in wave order and write the normalised output. Each lane owns 8
+// consecutive output values of one query head; the states are read four at
+// a time with their loads issued together. A wave whose range starts before
+// the sequence holds its state in its second slot, every other wave in its
+// first.
+template <int DT, int D>
+__device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int64_t first,
+                               int64_t last, int64_t total) {
+  const int lane = threadIdx.x;
+  const int32_t G = p.group;
+  const int32_t W = p.num_waves;
+  const int64_t out_row = ((int64_t)s * p.num_q_heads + (int64_t)g * G) * D;
+  const int32_t w0 = wave_of(first, total, W), w1 = wave_of(last, total, W);
+  const int32_t stride = G * (D + 4);
+  for (int32_t e = 8 * lane; e < G * D; e += 512) {
+    const int32_t h = e / D;
+    float mx = -INFINITY, den = 0.f;
+    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int32_t wv = w0;
+    while (wv <= w1) {
+      int32_t slot[4];
+      int cnt = 0;
+      for (; wv <= w1 && cnt < 4; ++wv) {
+        if (wave_empty(wv, total, W)) continue;
+        slot[cnt++] = 2 * wv + (total * wv / W < first ? 1 : 0);
+      }
+      float4 o0[4], o1[4];
+      float mk[4], lk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < cnt) {
+          const float* base = p.ws_partial + (int64_t)slot[k] * stride;
+          o0[k] = *reinterpret_cast<const float4*>(base + e);
+          o1[k] = *reinterpret_cast<const float4*>(base + e + 4);
+          mk[k] = base[G * D + h];
+          lk[k] = base[G * D + G + h];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < cnt) {
+          const float m_new = fmaxf(mx, mk[k]);
+          const float so = __builtin_amdgcn_exp2f(mx - m_new);
+          const float sk = __builtin_amdgcn_exp2f(mk[k] - m_new);
+          den = den * so + lk[k] * sk;
+          const float ov[8] = {o0[k].x, o0[k].y, o0[k].z, o0[k].w, o1[k].x, o1[k].y, o1[k].z, o1[k].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) num[i] = num[i] * so + ov[i] * sk;
+          mx = m_new;
+        }
+      }
+    }
+    const float inv = 1.0f / den;
+    if constexpr (DT == PKV_BF16) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        bf16x2 v = {(__bf16)(num[i] * inv), (__bf16)(num[i + 1] * inv)};
+        wd[i / 2] = __builtin_bit_cast(uint32_t, v);
+      }
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + out_row + e) =
+          uint4{wd[0], wd[1], wd[2], wd[3]};
+    } else {
+      float* o = reinterpret_cast<float*>(p.out) + out_row + e;
+      *reinterpret_cast<float4*>(o) = float4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+      *reinterpret_cast<float4*>(o + 4) = float4{num[4] * inv, num[5] * inv, num[6] * inv, num[7] * inv};
+    }
+  }
+}
+
+// Tiles in flight per wave: a multiple of 2; the register budget allows two
+// waves per SIMD up to depth 4 and one beyond.
+template <int DT, int D, int DEPTH>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(DEPTH <= 4 ? 2 : 1)))
 decode_split_kernel(DecodeParams p) {
   using Sh = Shape<DT, D>;
+  __shared__ int32_t s_ids[kIds];
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int kg = lane >> 4;
@@ -300,16 +412,32 @@ decode_split_kernel(DecodeParams p) {
   const int32_t w = (hw % kXcds) * per_xcd + hw / kXcds;
 
   // Total tiles per head: scan the block counts in chunks of 64 sequences.
+  // The first chunk's scan is kept: with up to 64 sequences it also serves
+  // to locate the wave's first tile without reading the lengths again.
   int32_t per_head = 0;
+  int32_t nb0 = 0, incl0 = 0, len0 = 0;
   for (int32_t base = 0; base < p.num_seqs; base += 64) {
-    const int32_t s = base + lane;
-    const int32_t nb = s < p.num_seqs ? (seq_len_clamped(p, s) + 15) >> 4 : 0;
+    const int32_t sq = base + lane;
+    const int32_t len = sq < p.num_seqs ? seq_len_clamped(p, sq) : 0;
+    const int32_t nb = (len + 15) >> 4;
     const int32_t incl = wave_incl_scan(nb);
-    if (hw == 0) {
-      if (s < p.num_seqs) p.ws_prefix[s + 1] = per_head + incl;
-      if (base == 0 && lane == 0) p.ws_prefix[0] = 0;
+    if (base == 0) {
+      nb0 = nb;
+      incl0 = incl;
+      len0 = len;
     }
-    per_head += __shfl(incl, 63);
+    if (hw == 0) {
+      if (sq < p.num_seqs) p.ws_prefix[sq + 1] = per_head + incl;
+      if (base == 0 && lane == 0) p.ws_prefix[0] = 0;
+      // Empty sequences own no tile: this wave writes their zero output.
+      uint64_t empty = __ballot(sq < p.num_seqs && len == 0);
+      while (empty) {
+        const int li = __builtin_ctzll(empty);
+        empty &= empty - 1;
+        zero_rows<DT, D>(p, base + li);
+      }
+    }
+    per_head += __builtin_amdgcn_readlane(incl, 63);
   }
   const int64_t total = (int64_t)per_head * p.num_kv_heads;
   const int64_t i0 = total * w / p.num_waves;
@@ -319,25 +447,29 @@ decode_split_kernel(DecodeParams p) {
   // Locate the (head, sequence) holding tile i0.
   int32_t g = (int32_t)(i0 / per_head);
   const int32_t r = (int32_t)(i0 - (int64_t)g * per_head);
-  int32_t s = 0, seq_start = 0;
+  int32_t s = 0, seq_start = 0, len_s = 0;
   {
     int32_t start = 0;
     for (int32_t base = 0; base < p.num_seqs; base += 64) {
-      const int32_t sq = base + lane;
-      const int32_t nb = sq < p.num_seqs ? (seq_len_clamped(p, sq) + 15) >> 4 : 0;
-      const int32_t incl = wave_incl_scan(nb);
+      int32_t nb = nb0, incl = incl0, len = len0;
+      if (base > 0) {
+        const int32_t sq = base + lane;
+        len = sq < p.num_seqs ? seq_len_clamped(p, sq) : 0;
+        nb = (len + 15) >> 4;
+        incl = wave_incl_scan(nb);
+      }
       const uint64_t hit = __ballot(start + incl > r);
       if (hit) {
         const int li = __builtin_ctzll(hit);
         s = base + li;
-        seq_start = start + __shfl(incl - nb, li);
+        seq_start = start + __builtin_amdgcn_readlane(incl - nb, li);
+        len_s = __builtin_amdgcn_readlane(len, li);
         break;
       }
-      start += __shfl(incl, 63);
+      start += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   int32_t j0 = r - seq_start;
-  int32_t len_s = seq_len_clamped(p, s);
   int32_t nb_s = (len_s + 15) >> 4;
 
   const uint32_t k_off = (uint32_t)(n * Sh::kRow + kg * 16);
@@ -371,41 +503,45 @@ decode_split_kernel(DecodeParams p) {
       const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks;
       const char* kbase = p.k_cache + (int64_t)g * head_stride;
       const char* vbase = p.v_cache + (int64_t)g * head_stride;
-      // Block ids of the piece, 64 at a time: lane i holds block j0c + i.
-      int32_t idc = j0;
-      int32_t ids = 0;
-      {
-        const int32_t jj = min(idc + lane, j1 - 1);
-        ids = trow[jj];
-      }
-      auto block_of = [&](int32_t j) -> int32_t {
-        if (j >= idc + 64) {
-          idc = j;
-          const int32_t jj = min(idc + lane, j1 - 1);
-          ids = trow[jj];
+      // Sub-pieces of up to kIds blocks: their block ids are staged in LDS
+      // first, so the loop reads ids with LDS loads that never wait on the
+      // K/V loads in flight.
+      for (int32_t c0 = j0; c0 < j1; c0 += kIds) {
+        const int32_t c1 = min(c0 + kIds, j1);
+        __syncthreads();
+        for (int32_t i = lane; i < c1 - c0; i += 64) {
+          const int32_t b = trow[c0 + i];
+          s_ids[i] = (uint32_t)b < (uint32_t)p.num_blocks ? b : 0;
         }
-        int32_t b = __builtin_amdgcn_readlane(ids, j - idc);
-        return (uint32_t)b < (uint32_t)p.num_blocks ? b : 0;
-      };
-
-      Tile<DT, D> buf[Sh::kDepth];
+        __syncthreads();
+        auto block_of = [&](int32_t j) -> int64_t {
+          return __builtin_amdgcn_readfirstlane(s_ids[min(j, c1 - 1) - c0]);
+        };
+        Tile<DT, D> buf[DEPTH];
+        // Tiles are issued in order (the scheduler must not interleave
+        // them): the waits below count loads in issue order.
 #pragma unroll
-      for (int u = 0; u < Sh::kDepth; ++u) {
-        const int32_t b = block_of(min(j0 + u, j1 - 1));
-        load_tile<DT, D>(buf[u], kbase + (int64_t)b * block_stride, vbase + (int64_t)b * block_stride,
-                         k_off, v_off);
-      }
-      for (int32_t jb = j0; jb < j1; jb += Sh::kDepth) {
+        for (int u = 0; u < DEPTH; ++u) {
+          const int64_t b = block_of(c0 + u);
+          load_tile<DT, D>(buf[u], kbase + b * block_stride, vbase + b * block_stride, k_off, v_off);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int32_t jb = c0; jb < c1; jb += DEPTH) {
 #pragma unroll
-        for (int u = 0; u < Sh::kDepth; ++u) {
-          const int32_t j = jb + u;
-          if (j < j1) {
-            const int32_t valid = min(16, len_s - 16 * j);
+          for (int u = 0; u < DEPTH; ++u) {
+            const int32_t j = jb + u;
+            // Tiles past the end of the sub-piece (at most DEPTH-1) are
+            // fully masked: they leave m, l and o unchanged. Keeping the
+            // body free of branches keeps the compiler's wait counts exact.
+            const int32_t valid = j < c1 ? min(16, len_s - 16 * j) : 0;
             attend_block<DT, D>(st, buf[u], qv, p.scale_log2, valid, kg);
+            // Always issue the next load (the last block again past the
+            // end) for the same reason.
+            const int64_t b = block_of(j + DEPTH);
+            load_tile<DT, D>(buf[u], kbase + b * block_stride, vbase + b * block_stride, k_off,
+                             v_off);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          const int32_t b = block_of(min(j + Sh::kDepth, j1 - 1));
-          load_tile<DT, D>(buf[u], kbase + (int64_t)b * block_stride,
-                           vbase + (int64_t)b * block_stride, k_off, v_off);
         }
       }
       if (j0 == 0 && j1 == nb_s) {
@@ -423,15 +559,16 @@ decode_split_kernel(DecodeParams p) {
       s = 0;
       ++g;
     }
-    len_s = seq_len_clamped(p, s);
+    len_s = seq_len_uniform(p, s);
     nb_s = (len_s + 15) >> 4;
     j0 = 0;
   }
 }
 
-// Merge the partial states of sequences whose tiles were split across
-// waves, and zero the output of empty sequences. One workgroup per
-// (sequence, KV head).
+// Merge the partial states of every sequence whose tiles were split across
+// waves. One wave per (sequence, KV head); sequences held by a single wave
+// (written directly) and empty sequences (zeroed by the split kernel) are
+// skipped.
 template <int DT, int D>
 __global__ void __launch_bounds__(64)
 decode_merge_kernel(DecodeParams p) {
@@ -440,70 +577,47 @@ decode_merge_kernel(DecodeParams p) {
   const int32_t per_head = p.ws_prefix[p.num_seqs];
   const int32_t a = p.ws_prefix[s];
   const int32_t b = p.ws_prefix[s + 1];
-  const int lane = threadIdx.x;
-  const int32_t G = p.group;
-  const int64_t out_row = ((int64_t)s * p.num_q_heads + (int64_t)g * G) * D;
-  if (a == b) {  // empty sequence: zero output
-    for (int32_t e = lane; e < G * D; e += 64) {
-      if constexpr (DT == PKV_BF16)
-        reinterpret_cast<uint16_t*>(p.out)[out_row + e] = 0;
-      else
-        reinterpret_cast<float*>(p.out)[out_row + e] = 0.f;
-    }
-    return;
-  }
+  if (a == b) return;
   const int64_t total = (int64_t)per_head * p.num_kv_heads;
   const int64_t first = (int64_t)g * per_head + a;
   const int64_t last = (int64_t)g * per_head + b - 1;
-  // wave covering tile i: largest w with floor(w*total/W) <= i
-  const int32_t W = p.num_waves;
-  const int32_t w0 = (int32_t)(((first + 1) * W + total - 1) / total - 1);
-  const int32_t w1 = (int32_t)(((last + 1) * W + total - 1) / total - 1);
-  if (w0 == w1) return;  // written directly by its wave
-  const int32_t stride = G * (D + 4);
-  // Waves w0..w1 overlap the sequence; those with an empty range (possible
-  // when there are fewer tiles than waves) wrote nothing and are skipped.
-  // A wave whose range starts before the sequence holds it in its second
-  // slot, every other one in its first.
-  for (int32_t e = lane; e < G * D; e += 64) {
-    const int32_t h = e / D;
-    float mmax = -INFINITY;
-    for (int32_t w = w0; w <= w1; ++w) {
-      const int64_t st = total * w / W;
-      if (st == total * (w + 1) / W) continue;
-      const int32_t slot = 2 * w + (st < first ? 1 : 0);
-      mmax = fmaxf(mmax, p.ws_partial[(int64_t)slot * stride + G * D + h]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int32_t w = w0; w <= w1; ++w) {
-      const int64_t st = total * w / W;
-      if (st == total * (w + 1) / W) continue;
-      const int32_t slot = 2 * w + (st < first ? 1 : 0);
-      const float* base = p.ws_partial + (int64_t)slot * stride;
-      const float sc = __builtin_amdgcn_exp2f(base[G * D + h] - mmax);
-      num += sc * base[e];
-      den += sc * base[G * D + G + h];
-    }
-    const float o = num / den;
-    if constexpr (DT == PKV_BF16) {
-      bf16x2 v = {(__bf16)o, (__bf16)0.0f};
-      reinterpret_cast<uint16_t*>(p.out)[out_row + e] =
-          (uint16_t)(__builtin_bit_cast(uint32_t, v) & 0xFFFFu);
-    } else {
-      reinterpret_cast<float*>(p.out)[out_row + e] = o;
-    }
-  }
+  if (wave_of(first, total, p.num_waves) == wave_of(last, total, p.num_waves)) return;
+  merge_sequence<DT, D>(p, s, g, first, last, total);
 }
 
 int g_waves_device = -1;
 int g_waves = 0;
 
+int g_depth = 0;
+
+int decode_depth() {
+  if (g_depth == 0) {
+    int d = 2;
+    if (const char* env = getenv("PKV_DECODE_DEPTH")) {
+      int v = atoi(env);
+      if (v == 2 || v == 4 || v == 8) d = v;
+    }
+    g_depth = d;
+  }
+  return g_depth;
+}
+
 template <int DT, int D>
-hipError_t launch(const DecodeParams& prm, int32_t seqs_heads, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<DT, D>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+hipError_t launch(const DecodeParams& prm, hipStream_t stream) {
+  // 512-byte rows (fp32, head_dim 128) only fit two tiles in flight.
+  const int depth = Shape<DT, D>::kRow > 256 ? 2 : decode_depth();
+  if constexpr (Shape<DT, D>::kRow > 256) {
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+  } else if (depth == 2)
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+  else if (depth == 8)
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 8>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 4>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(seqs_heads), dim3(64), 0, stream, prm);
+  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(prm.num_seqs * prm.num_kv_heads), dim3(64),
+                     0, stream, prm);
   return hipGetLastError();
 }
 
@@ -517,7 +631,7 @@ int decode_num_waves() {
   if (dev != g_waves_device) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
-    int per_cu = 8;
+    int per_cu = 2;
     if (const char* env = getenv("PKV_DECODE_WAVES_PER_CU")) {
       int v = atoi(env);
       if (v >= 1 && v <= 32) per_cu = v;
@@ -530,9 +644,15 @@ int decode_num_waves() {
   return g_waves;
 }
 
+// Workspace: [block-count prefix sums, num_seqs + 1 int32, padded to 256 B]
+// [partial states, 2 per wave].
+static size_t prefix_bytes(int32_t num_seqs) {
+  return ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256;
+}
+
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim) {
-  const size_t prefix = ((size_t)(num_seqs + 1) * 4 + 255) / 256 * 256;
+  const size_t prefix = prefix_bytes(num_seqs);
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
   const size_t partial = 2 * (size_t)decode_num_waves() * group * (head_dim + 4) * 4;
   return prefix + partial;
@@ -547,7 +667,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.block_table = a.block_table;
   p.context_lens = a.context_lens;
   p.ws_prefix = reinterpret_cast<int32_t*>(a.workspace);
-  const size_t prefix = ((size_t)(a.num_seqs + 1) * 4 + 255) / 256 * 256;
+  const size_t prefix = prefix_bytes(a.num_seqs);
   p.ws_partial = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + prefix);
   p.num_seqs = a.num_seqs;
   p.num_blocks = a.num_blocks;
@@ -557,11 +677,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.num_q_heads / a.num_kv_heads;
   p.num_waves = decode_num_waves();
   p.scale_log2 = a.scale * kLog2e;
-  const int32_t sh = a.num_seqs * a.num_kv_heads;
   if (a.dtype == PKV_BF16) {
-    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, sh, stream) : launch<PKV_BF16, 64>(p, sh, stream);
+    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, stream) : launch<PKV_BF16, 64>(p, stream);
   }
-  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, sh, stream) : launch<PKV_F32, 64>(p, sh, stream);
+  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream) : launch<PKV_F32, 64>(p, stream);
 }
 
 }  // namespace pkv

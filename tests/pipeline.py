@@ -115,8 +115,7 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
         table, lens = a.block_table(sids, maxb)
         q = torch.cat([w.seq_q(s) for s in dec]).to(device)
         out = torch.empty_like(q)
-        ws = torch.empty(pkv.decode_workspace_size(len(dec), w.num_q_heads, w.num_kv_heads,
-                                                   w.head_dim), dtype=torch.uint8, device=device)
+        ws = pkv.decode_workspace(len(dec), w.num_q_heads, w.num_kv_heads, w.head_dim, device)
         pkv.decode(out, q, kc, vc, torch.from_numpy(table).to(device),
                    torch.from_numpy(lens).to(device), w.scale, ws)
         res["decode"] = out

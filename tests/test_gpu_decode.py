@@ -208,10 +208,29 @@ def test_decode_bad_block_ids_are_clamped():
     table = torch.tensor([[1, 10 ** 6], [-5, 2]], dtype=torch.int32, device="cuda")
     lens = torch.tensor([30, 10 ** 6], dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
-    ws = torch.empty(pkv.decode_workspace_size(2, 4, hkv, d), dtype=torch.uint8, device="cuda")
+    ws = pkv.decode_workspace(2, 4, hkv, d)
     pkv.decode(out, q, kc, vc, table, lens, 0.1, ws)
     torch.cuda.synchronize()
     assert torch.allclose(out, torch.ones_like(out))
+
+
+def test_decode_workspace_shared_across_calls():
+    """One workspace serves consecutive calls of different shapes."""
+    _announce("decode workspace reuse")
+    wls = [workloads.custom("ws%d" % i, 40 + i, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                            dtype="bf16")
+           for i, lens in enumerate([[3000, 20, 900], [64, 64, 64, 64, 2000], [5000]])]
+    ws = pkv.decode_workspace(8, 32, 8, 128)
+    for rep in range(2):
+        for w in wls:
+            nat = run_native(w, prefill=False)
+            dec = w.decode_seqs
+            q = torch.cat([w.seq_q(s) for s in dec]).cuda()
+            out = torch.empty_like(q)
+            pkv.decode(out, q, nat["k_cache"], nat["v_cache"], torch.from_numpy(nat["decode_table"]).cuda(),
+                       torch.from_numpy(nat["decode_lens"]).cuda(), w.scale, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), nat["decode"].view(torch.int16))
 
 
 def test_decode_workspace_too_small():
