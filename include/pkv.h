@@ -224,7 +224,9 @@ int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_
  * sequence's total length including the chunk (the chunk's K/V are already
  * in the pool), so query i of the chunk sits at position
  * p = context_lens[c] - q_len_c + i and attends to positions 0..p.
- * q, out: device [cu_q_lens[num_chunks]][num_q_heads][head_dim] in `dtype`.
+ * q, out: device [total_q][num_q_heads][head_dim] in `dtype`; total_q is
+ * normally cu_q_lens[num_chunks] (rows a chunk would place at or beyond
+ * total_q are not computed, never read or written).
  * cu_q_lens: device int32 [num_chunks+1], non-decreasing from 0.
  * context_lens: device int32 [num_chunks]. block_table: device int32
  * [num_chunks][max_blocks_per_seq]. max_q_len bounds every chunk's length
@@ -233,7 +235,7 @@ int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                                       const int32_t* context_lens, const int32_t* block_table,
                                       const void* k_cache, const void* v_cache,
-                                      int32_t num_chunks, int32_t num_blocks,
+                                      int32_t num_chunks, int32_t total_q, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_q_len,
                                       int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t head_dim, float scale, int32_t dtype,

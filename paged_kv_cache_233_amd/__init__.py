@@ -77,8 +77,8 @@ _SIGNATURES = {
     "pkv_prefill_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     ctypes.POINTER(_c_sz)], ctypes.c_int),
     "pkv_paged_attention_prefill_chunk": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
-                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
-                                           _c_i32, _c_p, _c_sz, _c_p], ctypes.c_int),
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p], ctypes.c_int),
 }
 
 
@@ -362,6 +362,6 @@ def prefill_chunk(out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache
     _check(library().pkv_paged_attention_prefill_chunk(
         _dev(out, "out"), _dev(q, "q"), _dev(cu_q_lens, "cu_q_lens", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), _dev(block_table, "block_table", torch.int32),
-        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), c, nb, int(block_table.shape[1]),
-        int(max_q_len), int(q.shape[1]), hkv, d, float(scale), _dtype_code(q), ws_ptr, ws_bytes,
-        _stream(stream)))
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), c, int(q.shape[0]), nb,
+        int(block_table.shape[1]), int(max_q_len), int(q.shape[1]), hkv, d, float(scale),
+        _dtype_code(q), ws_ptr, ws_bytes, _stream(stream)))

@@ -169,7 +169,7 @@ int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                                       const int32_t* context_lens, const int32_t* block_table,
                                       const void* k_cache, const void* v_cache,
-                                      int32_t num_chunks, int32_t num_blocks,
+                                      int32_t num_chunks, int32_t total_q, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_q_len,
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       float scale, int32_t dtype, void* workspace,
@@ -179,17 +179,19 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
   pkv::clear_error();
   if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
-  if (num_chunks < 0 || num_blocks <= 0 || max_blocks_per_seq < 0 || max_q_len < 0)
+  if (num_chunks < 0 || total_q < 0 || num_blocks <= 0 || max_blocks_per_seq < 0 || max_q_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
-  if (num_chunks == 0 || max_q_len == 0) return PKV_OK;
+  if (num_chunks == 0 || max_q_len == 0 || total_q == 0) return PKV_OK;
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "q, out and pools must be 16-byte aligned");
   if (!out || !q || !cu_q_lens || !context_lens || !k_cache || !v_cache ||
       (!block_table && max_blocks_per_seq > 0))
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
   if ((int64_t)num_chunks * num_kv_heads * ((max_q_len + 15) / 16) > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARG, "grid too large");
   pkv::PrefillArgs a{out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache, num_chunks,
-                     num_blocks, max_blocks_per_seq, max_q_len, num_q_heads, num_kv_heads,
-                     head_dim, scale, dtype};
+                     total_q, num_blocks, max_blocks_per_seq, max_q_len, num_q_heads,
+                     num_kv_heads, head_dim, scale, dtype};
   hipError_t err = pkv::launch_prefill(a, (hipStream_t)stream);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "prefill launch");
 }

@@ -24,190 +24,20 @@
 // back the whole L2 of an XCD and costs far more than the second launch.)
 //
 // Per 16-token block and KV head the wave loads the K tile and the V tile
-// ([16][head_dim] each, contiguous) straight into registers and runs:
-//   S[t][n] = sum_d K[t][d] Q[n][d]           (MFMA, tokens x query heads)
-//   online softmax over t per head n         (exp2, cross-lane max/sum)
-//   O^T[d][n] += sum_t V[t][d] P[n][t]        (MFMA, head_dim x query heads)
-// The G query heads of the group fill G of the 16 MFMA columns; the other
-// columns carry zero queries and are never stored. Register layouts (lane l,
-// n = l % 16, kg = l / 16):
-//   K operand: row t = n of the tile, a 64-byte piece per load (kg picks the
-//              16-byte quarter), so each load instruction reads 16 rows x 64 B.
-//   S result : lane (n, kg) holds S[4kg + i][n], i = 0..3.
-//   V operand: lane reads row 4kg + j (j = 0..3), bytes [n*R/16, (n+1)*R/16)
-//              of the R-byte row, so each load instruction reads 4 whole rows.
-//   O result : lane (n, kg) holds head n, dims (4kg + i) * (D/16) + e.
+// straight into registers and runs the MFMA tile step of tile_attn.h; the G
+// query heads of the group fill G of the 16 MFMA columns, the other columns
+// carry zero queries and are never stored.
 #include <cstdlib>
 
 #include "internal.h"
+#include "tile_attn.h"
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
+using namespace pkv::tile;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;        // workgroups are dealt round-robin over 8 XCDs
 constexpr int kIds = 1024;      // block ids staged in LDS per sub-piece
-
-template <int DT, int D>
-struct Shape {
-  static constexpr int kElem = DT == PKV_F32 ? 4 : 2;
-  static constexpr int kRow = D * kElem;       // bytes of one token row of one head
-  static constexpr int kKLoads = kRow / 64;    // 16-byte K loads per lane per tile
-  static constexpr int kVWords = kRow / 64;    // 32-bit V words per lane per row
-  static constexpr int kTiles = D / 16;        // 16-row MFMA tiles of head_dim
-  static constexpr int kTileBytes = 16 * kRow; // one (block, head) tile
-};
-
-template <int DT, int D>
-struct Tile {
-  uint4 k[Shape<DT, D>::kKLoads];
-  uint32_t v[4][Shape<DT, D>::kVWords];
-};
-
-template <int W>
-__device__ __forceinline__ void load_words(uint32_t* dst, const char* p) {
-  if constexpr (W == 2) {
-    uint2 x = *reinterpret_cast<const uint2*>(p);
-    dst[0] = x.x;
-    dst[1] = x.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < W; i += 4) {
-      uint4 x = *reinterpret_cast<const uint4*>(p + 4 * i);
-      dst[i] = x.x;
-      dst[i + 1] = x.y;
-      dst[i + 2] = x.z;
-      dst[i + 3] = x.w;
-    }
-  }
-}
-
-template <int DT, int D>
-__device__ __forceinline__ void load_tile(Tile<DT, D>& tl, const char* kb, const char* vb,
-                                          uint32_t k_off, uint32_t v_off) {
-  using Sh = Shape<DT, D>;
-#pragma unroll
-  for (int c = 0; c < Sh::kKLoads; ++c)
-    tl.k[c] = *reinterpret_cast<const uint4*>(kb + k_off + 64 * c);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) load_words<Sh::kVWords>(tl.v[j], vb + v_off + j * Sh::kRow);
-}
-
-// Reductions over the four lanes l, l^16, l^32, l^48 (the four token groups
-// of one head). The gfx950 row-swap instructions hand each lane the value of
-// its partner 16 (then 32) lanes away in a VALU operation, so the loop has no
-// LDS traffic and no LDS wait. The combine is commutative, so all four lanes
-// end with the same bits.
-__device__ __forceinline__ float wave_max_kg(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float wave_sum_kg(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ float bf16_round(float x) {
-  bf16x2 p = {(__bf16)x, (__bf16)0.0f};
-  return (float)p[0];
-}
-
-// Running softmax state of one lane: head n = lane % 16.
-template <int DT, int D>
-struct State {
-  float m;                                  // running max of scaled scores (log2 units)
-  float l;                                  // running sum of weights
-  f32x4 o[Shape<DT, D>::kTiles];            // unnormalised output, see layout above
-};
-
-// One 16-token block. `valid` = number of tokens of the block inside the
-// context (1..16).
-template <int DT, int D>
-__device__ __forceinline__ void attend_block(State<DT, D>& st, Tile<DT, D>& tl,
-                                             const uint4* qv, float scale_log2, int valid,
-                                             int kg) {
-  using Sh = Shape<DT, D>;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (DT == PKV_BF16) {
-#pragma unroll
-    for (int c = 0; c < Sh::kKLoads; ++c)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tl.k[c]),
-                                                  __builtin_bit_cast(bf16x8, qv[c]), s, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int c = 0; c < Sh::kKLoads; ++c) {
-      const float* kf = reinterpret_cast<const float*>(&tl.k[c]);
-      const float* qf = reinterpret_cast<const float*>(&qv[c]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qf[e], s, 0, 0, 0);
-    }
-  }
-  float x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = s[i] * scale_log2;
-  if (valid < 16) {  // wave-uniform: only the last block of a sequence
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * kg + i >= valid) x[i] = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * kg + j >= valid) {
-#pragma unroll
-        for (int w = 0; w < Sh::kVWords; ++w) tl.v[j][w] = 0u;
-      }
-  }
-  const float bmax = wave_max_kg(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  const float m_new = fmaxf(st.m, bmax);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-  if constexpr (DT == PKV_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = bf16_round(p[i]);  // the weights the MFMA sees
-  }
-  const float rsum = wave_sum_kg((p[0] + p[1]) + (p[2] + p[3]));
-  st.l = st.l * alpha + rsum;
-  st.m = m_new;
-  if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-    for (int e = 0; e < Sh::kTiles; ++e) st.o[e] *= alpha;
-  }
-  if constexpr (DT == PKV_BF16) {
-    bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]};
-    bf16x2 p23 = {(__bf16)p[2], (__bf16)p[3]};
-    uint2 pb = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    const i16x4 b = __builtin_bit_cast(i16x4, pb);
-#pragma unroll
-    for (int e = 0; e < Sh::kTiles; ++e) {
-      // element e of each of the 4 rows this lane loaded, packed as 4 bf16
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint2 a;
-      a.x = __builtin_amdgcn_perm(tl.v[1][w], tl.v[0][w], sel);
-      a.y = __builtin_amdgcn_perm(tl.v[3][w], tl.v[2][w], sel);
-      st.o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), b,
-                                                          st.o[e], 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < Sh::kTiles; ++e)
-        st.o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, tl.v[j][e]), p[j],
-                                                       st.o[e], 0, 0, 0);
-    }
-  }
-}
 
 struct DecodeParams {
   void* out;
@@ -251,39 +81,6 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
     if (lane >= d) x += y;
   }
   return x;
-}
-
-template <int DT, int D>
-__device__ __forceinline__ void write_output(const DecodeParams& p, const State<DT, D>& st,
-                                             int32_t s, int32_t g, int n, int kg) {
-  using Sh = Shape<DT, D>;
-  if (n >= p.group) return;
-  const float inv = 1.0f / st.l;
-  const int64_t row = ((int64_t)s * p.num_q_heads + g * p.group + n) * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d0 = (4 * kg + i) * Sh::kTiles;
-    if constexpr (DT == PKV_BF16) {
-      uint32_t w[Sh::kTiles / 2];
-#pragma unroll
-      for (int e = 0; e < Sh::kTiles; e += 2) {
-        bf16x2 v = {(__bf16)(st.o[e][i] * inv), (__bf16)(st.o[e + 1][i] * inv)};
-        w[e / 2] = __builtin_bit_cast(uint32_t, v);
-      }
-      char* dst = reinterpret_cast<char*>(p.out) + (row + d0) * 2;
-      if constexpr (Sh::kTiles == 8) {
-        *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
-      } else {
-        *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
-      }
-    } else {
-      float* dst = reinterpret_cast<float*>(p.out) + row + d0;
-#pragma unroll
-      for (int e = 0; e < Sh::kTiles; e += 4)
-        *reinterpret_cast<float4*>(dst + e) =
-            float4{st.o[e][i] * inv, st.o[e + 1][i] * inv, st.o[e + 2][i] * inv, st.o[e + 3][i] * inv};
-    }
-  }
 }
 
 template <int DT, int D>
@@ -472,8 +269,8 @@ decode_split_kernel(DecodeParams p) {
   int32_t j0 = r - seq_start;
   int32_t nb_s = (len_s + 15) >> 4;
 
-  const uint32_t k_off = (uint32_t)(n * Sh::kRow + kg * 16);
-  const uint32_t v_off = (uint32_t)((4 * kg) * Sh::kRow + n * (Sh::kRow / 16));
+  const uint32_t k_off = k_lane_offset<DT, D>(n, kg);
+  const uint32_t v_off = v_lane_offset<DT, D>(n, kg);
   const int64_t head_stride = Sh::kTileBytes;
   const int64_t block_stride = (int64_t)p.num_kv_heads * Sh::kTileBytes;
 
@@ -483,22 +280,13 @@ decode_split_kernel(DecodeParams p) {
     const int32_t j1 = (int32_t)min((int64_t)nb_s, (int64_t)j0 + (i1 - i));
     if (j1 > j0) {
       // Query operand: head g*G + n for n < G, zero otherwise.
-      uint4 qv[Sh::kKLoads];
-      if (n < p.group) {
-        const char* qrow = reinterpret_cast<const char*>(p.q) +
-                           ((int64_t)s * p.num_q_heads + g * p.group + n) * Sh::kRow;
-#pragma unroll
-        for (int c = 0; c < Sh::kKLoads; ++c)
-          qv[c] = *reinterpret_cast<const uint4*>(qrow + 64 * c + 16 * kg);
-      } else {
-#pragma unroll
-        for (int c = 0; c < Sh::kKLoads; ++c) qv[c] = uint4{0u, 0u, 0u, 0u};
-      }
-      State<DT, D> st;
-      st.m = -INFINITY;
-      st.l = 0.f;
-#pragma unroll
-      for (int e = 0; e < Sh::kTiles; ++e) st.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      QOp<DT, D> qv[1];
+      load_query<DT, D>(qv[0],
+                        reinterpret_cast<const char*>(p.q) +
+                            ((int64_t)s * p.num_q_heads + g * p.group + n) * Sh::kRow,
+                        n < p.group, kg);
+      State<DT, D> st[1];
+      st[0].reset();
 
       const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks;
       const char* kbase = p.k_cache + (int64_t)g * head_stride;
@@ -533,8 +321,10 @@ decode_split_kernel(DecodeParams p) {
             // Tiles past the end of the sub-piece (at most DEPTH-1) are
             // fully masked: they leave m, l and o unchanged. Keeping the
             // body free of branches keeps the compiler's wait counts exact.
-            const int32_t valid = j < c1 ? min(16, len_s - 16 * j) : 0;
-            attend_block<DT, D>(st, buf[u], qv, p.scale_log2, valid, kg);
+            const int32_t t0 = 16 * j;
+            const int32_t end = j < c1 ? min(t0 + 16, len_s) : t0;  // valid: [t0, end)
+            const int lim[1] = {end - 1};
+            attend_tile<DT, D, 1>(st, buf[u], qv, p.scale_log2, t0, lim, end, end < t0 + 16, kg);
             // Always issue the next load (the last block again past the
             // end) for the same reason.
             const int64_t b = block_of(j + DEPTH);
@@ -545,9 +335,10 @@ decode_split_kernel(DecodeParams p) {
         }
       }
       if (j0 == 0 && j1 == nb_s) {
-        write_output<DT, D>(p, st, s, g, n, kg);
+        store_row<DT, D>(p.out, (int64_t)s * p.num_q_heads + g * p.group + n, st[0], kg,
+                         n < p.group);
       } else {
-        write_partial<DT, D>(p, st, 2 * w + (first_piece ? 0 : 1), n, kg);
+        write_partial<DT, D>(p, st[0], 2 * w + (first_piece ? 0 : 1), n, kg);
       }
       i += j1 - j0;
       first_piece = false;

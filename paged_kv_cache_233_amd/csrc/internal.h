@@ -67,6 +67,7 @@ struct PrefillArgs {
   const void* k_cache;
   const void* v_cache;
   int32_t num_chunks;
+  int32_t total_q;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t max_q_len;

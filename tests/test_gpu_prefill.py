@@ -1,0 +1,117 @@
+"""GPU parity of chunked-prefill attention against the CPU oracle, through
+the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_233_amd as pkv
+import workloads
+from tests.pipeline import assert_close, run_native, run_oracle, to_numpy_storage
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+# (cached tokens, chunk length) pairs: start at 0, mid-block, block-aligned,
+# single query, chunk longer than the cache, ragged tails
+CHUNKS = [(0, 5), (7, 12), (16, 3), (0, 1), (33, 64), (100, 37), (250, 130)]
+
+CASES = {
+    "bf16 d128 group 4": dict(num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16"),
+    "bf16 d128 group 1": dict(num_q_heads=4, num_kv_heads=4, head_dim=128, dtype="bf16"),
+    "bf16 d64 group 8": dict(num_q_heads=16, num_kv_heads=2, head_dim=64, dtype="bf16"),
+    "bf16 d128 group 16": dict(num_q_heads=32, num_kv_heads=2, head_dim=128, dtype="bf16"),
+    "bf16 d128 group 3": dict(num_q_heads=6, num_kv_heads=2, head_dim=128, dtype="bf16"),
+    "f32 d64 group 4": dict(num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="f32"),
+    "f32 d128 group 2": dict(num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_matches_oracle(name):
+    w = workloads.custom("pf", 50, [40, 300], chunks=CHUNKS, **CASES[name])
+    _announce("prefill %s" % name)
+    nat = run_native(w)
+    ora = run_oracle(w)
+    assert np.array_equal(nat["step_slots"], ora["step_slots"])
+    assert np.array_equal(nat["prefill_table"], ora["prefill_table"])
+    assert to_numpy_storage(nat["k_cache"]).tobytes() == ora["k_cache"].tobytes()
+    assert_close(nat["prefill"], ora["prefill"], w.dtype, name)
+    assert_close(nat["decode"], ora["decode"], w.dtype, name + " decode")
+
+
+def test_prefill_single_query_equals_decode():
+    """A one-query chunk at position p and a decode step with context p+1."""
+    _announce("prefill q_len 1 vs decode")
+    w = workloads.custom("pf1", 51, [], chunks=[(c, 1) for c in (0, 15, 16, 99, 700)],
+                         num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16")
+    nat = run_native(w)
+    q = torch.cat([w.seq_q(s) for s in w.chunk_seqs]).cuda()
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(q.shape[0], 32, 8, 128)
+    pkv.decode(out, q, nat["k_cache"], nat["v_cache"], torch.from_numpy(nat["prefill_table"]).cuda(),
+               torch.from_numpy(nat["prefill_lens"]).cuda(), w.scale, ws)
+    torch.cuda.synchronize()
+    ora = run_oracle(w)
+    assert_close(nat["prefill"], ora["prefill"], "bf16", "prefill")
+    assert_close(out, ora["prefill"], "bf16", "decode")
+
+
+def test_prefill_chunk_split_and_placement_invariance():
+    """One 200-token chunk equals two chunks of 120 and 80 at the right
+    offsets, bit for bit, and the result does not depend on where the blocks
+    sit in the pool."""
+    _announce("prefill invariance")
+    base = workloads.custom("pfs", 52, [], chunks=[(57, 200)], num_q_heads=32, num_kv_heads=8,
+                            head_dim=128, dtype="bf16")
+    nat = run_native(base)
+    full = nat["prefill"].cpu()
+    kc, vc = nat["k_cache"], nat["v_cache"]
+    table = torch.from_numpy(nat["prefill_table"]).cuda()
+    q = base.seq_q(base.chunk_seqs[0]).cuda()
+    # the same sequence queried as two chunks: rows 0..119 at context 57+120,
+    # rows 120..199 at context 257
+    out = torch.empty_like(q)
+    cu = torch.tensor([0, 120, 200], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([57 + 120, 257], dtype=torch.int32, device="cuda")
+    pkv.prefill_chunk(out, q, cu, lens, torch.cat([table, table]), kc, vc, 120, base.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), full.view(torch.int16))
+    # another physical placement of the same tokens
+    w2 = workloads.custom("pfs", 52, [], chunks=[(57, 200)], num_q_heads=32, num_kv_heads=8,
+                          head_dim=128, dtype="bf16")
+    w2.free_order = np.random.default_rng(9).permutation(np.arange(1, w2.num_blocks)).astype(np.int32)
+    nat2 = run_native(w2)
+    assert not np.array_equal(nat2["prefill_table"], nat["prefill_table"])
+    assert torch.equal(nat2["prefill"].cpu().view(torch.int16), full.view(torch.int16))
+
+
+def test_prefill_rows_beyond_total_q_untouched():
+    """cu_q_lens pointing past the query tensor: rows past total_q are neither
+    read nor written; the rows inside are computed."""
+    _announce("prefill bounds")
+    w = workloads.custom("pfb", 53, [], chunks=[(10, 20)], num_q_heads=8, num_kv_heads=2,
+                         head_dim=64, dtype="f32")
+    nat = run_native(w)
+    q = w.seq_q(w.chunk_seqs[0]).cuda()
+    out = torch.full_like(q, 7.0)
+    cu = torch.tensor([0, 1000], dtype=torch.int32, device="cuda")   # claims 1000 rows
+    lens = torch.tensor([30], dtype=torch.int32, device="cuda")
+    pkv.prefill_chunk(out, q, cu, lens, torch.from_numpy(nat["prefill_table"]).cuda(),
+                      nat["k_cache"], nat["v_cache"], 1000, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, nat["prefill"])
+
+
+def test_prefill_full_mixed_workload():
+    """The mixed workload's two 512-query chunks, launched as the step does."""
+    w = workloads.named("mixed")
+    _announce("prefill full mixed: chunks at %s" % [s.cached for s in w.chunk_seqs])
+    nat = run_native(w)
+    ora = run_oracle(w, decode_sample=[0, 9])
+    stats = assert_close(nat["prefill"], ora["prefill"], "bf16", "mixed prefill")
+    assert_close(nat["decode"][[0, 9]], ora["decode"], "bf16", "mixed decode")
+    print("mixed prefill error", stats)

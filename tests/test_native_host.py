@@ -229,8 +229,8 @@ def test_device_entry_points_reject_bad_arguments():
     assert _raw("pkv_paged_attention_decode", 16, 16, 16, 16, 16, 0, 1, 4, 1, 8, 2, 128,
                 ctypes.c_float(1.0), 1, 16, 1 << 20, None) == pkv.ERR_INVALID_ARG
     # prefill: bad head_dim
-    assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 4, 1, 1, 8, 2,
-                80, ctypes.c_float(1.0), 1, None, 0, None) == pkv.ERR_UNSUPPORTED
+    assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 1, 4, 1, 1, 8,
+                2, 80, ctypes.c_float(1.0), 1, None, 0, None) == pkv.ERR_UNSUPPORTED
     # copy_blocks: negative count
     assert _raw("pkv_copy_blocks", 16, 16, 16, -1, 4, 1, 128, 1, None) == pkv.ERR_INVALID_ARG
     assert b"head_dim" in pkv.library().pkv_last_error() or True
