@@ -33,9 +33,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 METRIC = "paged decode attention: KV-read HBM GB/s (% of peak) + tokens/s, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", "decode.hip")
+# the sources the decode kernels are built from (the traffic record names their hash)
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", f)
+               for f in ("decode.hip", "tile_attn.h")]
 
 
 def parse():
@@ -47,6 +50,7 @@ def parse():
     ap.add_argument("--pools", type=int, default=4, help="KV pool copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -68,7 +72,10 @@ def copy_probe():
 
 
 def kernel_source_hash():
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def load_traffic():
@@ -149,14 +156,17 @@ def main():
     v_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
     out = torch.empty_like(q)
     ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
-    # double-buffered pinned host staging for the per-step host->device copy
-    pin_slots = [torch.empty(S, dtype=torch.int64).pin_memory() for _ in range(2)]
-    pin_table = [torch.empty((S, maxb), dtype=torch.int32).pin_memory() for _ in range(2)]
-    pin_lens = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(2)]
+    # Per-step host->device staging: slots (int64 [S]), then context lengths
+    # (int32 [S]) and the block table (int32 [S, maxb]) in one pinned buffer,
+    # double buffered, copied with one transfer per step.
+    n32 = S + S * maxb
+    words = S + (n32 + 1) // 2
+    pinned = [torch.empty(words, dtype=torch.int64).pin_memory() for _ in range(2)]
     copied = [torch.cuda.Event(), torch.cuda.Event()]
-    d_slots = torch.empty(S, dtype=torch.int64, device=dev)
-    d_table = torch.empty((S, maxb), dtype=torch.int32, device=dev)
-    d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+    d_stage = torch.empty(words, dtype=torch.int64, device=dev)
+    d_slots = d_stage[:S]
+    d_lens = d_stage[S:].view(torch.int32)[:S]
+    d_table = d_stage[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
     pairs_buf = np.empty(2 * S, dtype=np.int64)
     kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     stream = torch.cuda.current_stream()
@@ -170,13 +180,12 @@ def main():
         b = t % 2
         if t >= 2:
             copied[b].synchronize()      # the copy that last read this staging buffer is done
-        npairs = alloc.batch_append_into(sids, ones, pin_slots[b].data_ptr(), pairs_buf)
+        base = pinned[b].data_ptr()
+        npairs = alloc.batch_append_into(sids, ones, base, pairs_buf)
         assert npairs == 0
-        alloc.fill_block_table_into(sids, pin_table[b].data_ptr(), maxb, pin_lens[b].data_ptr())
-        ctx_tokens.append(int(pin_lens[b].numpy().sum()))
-        d_slots.copy_(pin_slots[b], non_blocking=True)
-        d_table.copy_(pin_table[b], non_blocking=True)
-        d_lens.copy_(pin_lens[b], non_blocking=True)
+        alloc.fill_block_table_into(sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
+        ctx_tokens.append(int(pinned[b][S:].view(torch.int32)[:S].sum()))
+        d_stage.copy_(pinned[b], non_blocking=True)
         copied[b].record(stream)
         kc, vc = pools[t % len(pools)]
         e0, e1, e2 = ev[t]
@@ -205,6 +214,8 @@ def main():
     log("decode kernels: mean %.1f us (min %.1f, median %.1f); reshape_and_cache %.1f us; "
         "step %.1f us wall" % (dec_us.mean(), dec_us.min(), np.median(dec_us), rc_us.mean(),
                                ms_per_step * 1e3))
+
+    prefill = None if args.no_prefill else prefill_leg(args, dev)
 
     # ------------------------------------------------------- CPU oracle leg
     cpu = None
@@ -240,9 +251,67 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(),
                      "kernel": "paged_attention_decode (decode_split_kernel)"},
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def prefill_leg(args, dev):
+    """Chunked prefill on the mixed workload's two 512-query chunks (cached
+    prefixes of the seeded lengths), all K/V resident: kernel time, tokens/s
+    and MFMA throughput on the algorithmic FLOPs (unmasked query-key pairs
+    only: 4 * head_dim * query heads per pair)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    w = workloads.named("mixed")
+    ch = w.chunk_seqs
+    a = pkv.Allocator(w.num_blocks)
+    a.set_free_order(w.free_order)
+    shape = (w.num_blocks, w.num_kv_heads, 16, w.head_dim)
+    kc = torch.zeros(shape, dtype=w.torch_dtype, device=dev)
+    vc = torch.zeros_like(kc)
+    for spec in ch:
+        a.add(spec.seq_id)
+        slots, _ = a.append(spec.seq_id, spec.total)
+        k, v = w.seq_kv(spec)
+        pkv.reshape_and_cache(kc, vc, k.to(dev), v.to(dev), torch.from_numpy(slots).to(dev))
+    table, lens = a.block_table([s.seq_id for s in ch], w.max_blocks_per_seq())
+    qs = [w.seq_q(s) for s in ch]
+    cu = np.cumsum([0] + [x.shape[0] for x in qs]).astype(np.int32)
+    q = torch.cat(qs).to(dev)
+    out = torch.empty_like(q)
+    d_cu, d_lens = torch.from_numpy(cu).to(dev), torch.from_numpy(lens).to(dev)
+    d_table = torch.from_numpy(table).to(dev)
+    qmax = int(max(x.shape[0] for x in qs))
+    for _ in range(5):
+        pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax, w.scale)
+    reps = max(10, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax, w.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    pairs = 0
+    for spec in ch:
+        # queries at positions cached .. total-1 see position+1 keys each
+        pairs += sum(range(spec.cached + 1, spec.total + 1))
+    flops = 4.0 * w.head_dim * w.num_q_heads * pairs
+    tflops = flops / (us * 1e-6) / 1e12
+    log("prefill: %d chunks (cached %s, 512 queries each): %.1f us, %.1f TFLOP/s"
+        % (len(ch), [s.cached for s in ch], us, tflops))
+    return {"workload": "mixed: %d chunks of 512 queries over %s cached tokens, 32 q / 8 kv heads, "
+                        "head_dim 128, bf16" % (len(ch), [s.cached for s in ch]),
+            "kernel_us": round(us, 2), "query_tokens_per_s": round(int(cu[-1]) / (us * 1e-6), 1),
+            "algorithmic_gflop": round(flops / 1e9, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
 
 
 def cpu_baseline(w, nseq):
