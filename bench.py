@@ -172,8 +172,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     total_steps = args.warmup + args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(total_steps)]
     ctx_tokens = []
 
     def step(t):
@@ -188,12 +187,15 @@ def main():
         d_stage.copy_(pinned[b], non_blocking=True)
         copied[b].record(stream)
         kc, vc = pools[t % len(pools)]
-        e0, e1, e2 = ev[t]
+        e0, e1, e2, e3 = ev[t]
         e0.record(stream)
         pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots)
         e1.record(stream)
-        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws)
+        # decode = split-KV kernel, then merge kernel (timed apart)
+        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="split")
         e2.record(stream)
+        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="merge")
+        e3.record(stream)
 
     for t in range(args.warmup):
         step(t)
@@ -206,14 +208,18 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     timed = range(args.warmup, total_steps)
     rc_us = np.array([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in timed])
-    dec_us = np.array([ev[t][1].elapsed_time(ev[t][2]) * 1e3 for t in timed])
+    split_us = np.array([ev[t][1].elapsed_time(ev[t][2]) * 1e3 for t in timed])
+    merge_us = np.array([ev[t][2].elapsed_time(ev[t][3]) * 1e3 for t in timed])
+    dec_us = np.array([ev[t][1].elapsed_time(ev[t][3]) * 1e3 for t in timed])
     kv_bytes = np.array([ctx_tokens[t] * kv_bytes_per_token for t in timed], dtype=np.float64)
-    achieved = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
+    achieved = float(kv_bytes.mean() / (split_us.mean() * 1e-6) / 1e9)
+    achieved_op = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
     value = float(kv_bytes.sum() / wall / 1e9)
     tokens_per_s = S * args.steps / wall
-    log("decode kernels: mean %.1f us (min %.1f, median %.1f); reshape_and_cache %.1f us; "
-        "step %.1f us wall" % (dec_us.mean(), dec_us.min(), np.median(dec_us), rc_us.mean(),
-                               ms_per_step * 1e3))
+    log("decode kernels: mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
+        "reshape_and_cache %.1f us; step %.1f us wall"
+        % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(), merge_us.mean(),
+           rc_us.mean(), ms_per_step * 1e3))
 
     prefill = None if args.no_prefill else prefill_leg(args, dev)
 
@@ -246,11 +252,16 @@ def main():
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
                       "decode_median": round(float(np.median(dec_us)), 2),
+                      "decode_split_kernel_mean": round(float(split_us.mean()), 2),
+                      "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
                       "reshape_and_cache_mean": round(float(rc_us.mean()), 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(),
-                     "kernel": "paged_attention_decode (decode_split_kernel)"},
+                     "kernel": "decode_split_kernel (dominant kernel of paged_attention_decode)"},
+        "decode_op": {"kernels": "decode_split_kernel + decode_merge_kernel",
+                      "achieved_gbs": round(achieved_op, 2),
+                      "frac_of_hbm_peak": round(achieved_op / HBM_PEAK_GBS, 4)},
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -210,6 +210,27 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                float scale, int32_t dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* The two phases of pkv_paged_attention_decode, for callers that time or
+ * interleave them: the split-KV kernel (writes whole sequences' outputs and
+ * the partial states of split ones into the workspace), then the merge
+ * kernel (folds the partial states in token order, writes the remaining
+ * outputs). Called in that order on one stream with identical arguments and
+ * workspace, they produce exactly what pkv_paged_attention_decode produces. */
+int pkv_paged_attention_decode_split(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float scale, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float scale, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attention_prefill_chunk needs (0 if none). */
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,

@@ -74,6 +74,12 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
                                    ctypes.c_int),
+    "pkv_paged_attention_decode_split": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p,
+                                          _c_sz, _c_p], ctypes.c_int),
+    "pkv_paged_attention_decode_merge": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p,
+                                          _c_sz, _c_p], ctypes.c_int),
     "pkv_prefill_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     ctypes.POINTER(_c_sz)], ctypes.c_int),
     "pkv_paged_attention_prefill_chunk": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
@@ -314,10 +320,12 @@ def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_di
 
 
 def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, workspace,
-           stream=None) -> None:
+           stream=None, phase: str = "both") -> None:
     """Paged decode attention; q/out [S, Hq, D], block_table int32 [S, maxB],
     context_lens int32 [S], workspace a uint8 device tensor of at least
-    decode_workspace_size(...) bytes (``decode_workspace`` allocates one)."""
+    decode_workspace_size(...) bytes (``decode_workspace`` allocates one).
+    ``phase`` "split" or "merge" launches one of the two kernels only (call
+    both, in that order, for the full result)."""
     torch = _torch()
     nb, hkv, d = _pool_shape(k_cache)
     if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
@@ -327,7 +335,10 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
     s, hq = int(q.shape[0]), int(q.shape[1])
     if block_table.dim() != 2 or block_table.shape[0] != s or context_lens.numel() != s:
         raise Error(ERR_INVALID_ARG, "block_table must be [S, maxB] and context_lens [S]")
-    _check(library().pkv_paged_attention_decode(
+    fn = {"both": library().pkv_paged_attention_decode,
+          "split": library().pkv_paged_attention_decode_split,
+          "merge": library().pkv_paged_attention_decode_merge}[phase]
+    _check(fn(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),

@@ -122,12 +122,13 @@ int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return PKV_OK;
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_table, const int32_t* context_lens,
-                               int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
-                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                               float scale, int32_t dtype, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, const int32_t* context_lens, int32_t num_seqs,
+                 int32_t num_blocks, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
+                 void* workspace, size_t workspace_bytes, void* stream, int phases) {
   pkv::clear_error();
   if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
@@ -149,8 +150,45 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                     max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                     workspace};
-  hipError_t err = pkv::launch_decode(a, (hipStream_t)stream);
+  hipError_t err = pkv::launch_decode(a, phases, (hipStream_t)stream);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
+}
+
+}  // namespace
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float scale, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      workspace, workspace_bytes, stream, 3);
+}
+
+int pkv_paged_attention_decode_split(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float scale, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      workspace, workspace_bytes, stream, 1);
+}
+
+int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_table,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float scale, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      workspace, workspace_bytes, stream, 2);
 }
 
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,

@@ -37,7 +37,6 @@ namespace {
 using namespace pkv::tile;
 
 constexpr int kXcds = 8;        // workgroups are dealt round-robin over 8 XCDs
-constexpr int kIds = 1024;      // block ids staged in LDS per sub-piece
 
 struct DecodeParams {
   void* out;
@@ -55,6 +54,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t group;
   int32_t num_waves;
+  int32_t pieces_per_round;  // pieces whose query rows fit the LDS budget
   float scale_log2;
 };
 
@@ -194,19 +194,48 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int6
   }
 }
 
-// Tiles in flight per wave: a multiple of 2; the register budget allows two
-// waves per SIMD up to depth 4 and one beyond.
+// Piece of a wave's range: the tiles of one (sequence, KV head) it covers in
+// one round. Kept in LDS while the round streams.
+struct Piece {
+  int32_t s, g;        // sequence and KV head
+  int32_t j0;          // first block (of the sequence) in the piece
+  int32_t kstart;      // first flat tile index of the piece in the round
+  int32_t kend;        // one past its last flat tile index
+  int32_t len;         // clamped sequence length (tokens)
+  int32_t flags;       // kFinal | kWhole | kFirst | kCont
+  int32_t pad;
+};
+constexpr int32_t kFinal = 1;  // the wave's work on this sequence ends here
+constexpr int32_t kWhole = 2;  // the wave holds the whole sequence: store the output
+constexpr int32_t kFirst = 4;  // the sequence is the wave's first: partial state in slot 2w
+constexpr int32_t kCont = 8;   // continues the previous round's last piece: keep the state
+
+constexpr int kTilesPerRound = 512;
+constexpr int kPiecesPerRound = 16;
+
+// Split-KV decode. Each wave streams the tiles of its range as one flat list
+// (staged in LDS per round with the block ids resolved to pool tiles), so
+// the K/V load pipeline runs across sequence boundaries without draining;
+// the query rows of the round's pieces are staged in LDS too. The loop body
+// keeps the loads in issue order (the compiler's wait counts stay exact);
+// the last DEPTH-1 tiles of a round are computed in an epilogue without
+// further loads.
 template <int DT, int D, int DEPTH>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(DEPTH <= 4 ? 2 : 1)))
 decode_split_kernel(DecodeParams p) {
   using Sh = Shape<DT, D>;
-  __shared__ int32_t s_ids[kIds];
+  extern __shared__ __align__(16) char lds[];
+  int32_t* tiles = reinterpret_cast<int32_t*>(lds);                       // [kTilesPerRound]
+  Piece* pieces = reinterpret_cast<Piece*>(tiles + kTilesPerRound);       // [kPiecesPerRound]
+  char* qlds = reinterpret_cast<char*>(pieces + kPiecesPerRound);         // [kq][G * kRow]
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int kg = lane >> 4;
   const int32_t hw = blockIdx.x;
   const int32_t per_xcd = p.num_waves / kXcds;
   const int32_t w = (hw % kXcds) * per_xcd + hw / kXcds;
+  const int32_t G = p.group;
+  const int32_t qbytes = G * Sh::kRow;       // one piece's query rows
 
   // Total tiles per head: scan the block counts in chunks of 64 sequences.
   // The first chunk's scan is kept: with up to 64 sequences it also serves
@@ -266,93 +295,149 @@ decode_split_kernel(DecodeParams p) {
       start += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  int32_t j0 = r - seq_start;
-  int32_t nb_s = (len_s + 15) >> 4;
+  int32_t j = r - seq_start;             // next block of sequence s to take
 
   const uint32_t k_off = k_lane_offset<DT, D>(n, kg);
   const uint32_t v_off = v_lane_offset<DT, D>(n, kg);
-  const int64_t head_stride = Sh::kTileBytes;
-  const int64_t block_stride = (int64_t)p.num_kv_heads * Sh::kTileBytes;
+  const char* kpool = p.k_cache;
+  const char* vpool = p.v_cache;
 
+  QOp<DT, D> qv[1];
+  State<DT, D> st[1];
   int64_t i = i0;
-  bool first_piece = true;
+  bool first = true;                     // no piece finished yet: partial goes to slot 2w
+  bool cont = false;                     // the next round continues an open piece
+  int32_t open_j0 = 0;                   // first block the wave took of the open sequence
   while (i < i1) {
-    const int32_t j1 = (int32_t)min((int64_t)nb_s, (int64_t)j0 + (i1 - i));
-    if (j1 > j0) {
-      // Query operand: head g*G + n for n < G, zero otherwise.
-      QOp<DT, D> qv[1];
-      load_query<DT, D>(qv[0],
-                        reinterpret_cast<const char*>(p.q) +
-                            ((int64_t)s * p.num_q_heads + g * p.group + n) * Sh::kRow,
-                        n < p.group, kg);
-      State<DT, D> st[1];
-      st[0].reset();
-
-      const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks;
-      const char* kbase = p.k_cache + (int64_t)g * head_stride;
-      const char* vbase = p.v_cache + (int64_t)g * head_stride;
-      // Sub-pieces of up to kIds blocks: their block ids are staged in LDS
-      // first, so the loop reads ids with LDS loads that never wait on the
-      // K/V loads in flight.
-      for (int32_t c0 = j0; c0 < j1; c0 += kIds) {
-        const int32_t c1 = min(c0 + kIds, j1);
-        __syncthreads();
-        for (int32_t i = lane; i < c1 - c0; i += 64) {
-          const int32_t b = trow[c0 + i];
-          s_ids[i] = (uint32_t)b < (uint32_t)p.num_blocks ? b : 0;
+    // ---- build a round: pieces, their tiles and their query rows -------
+    int32_t nt = 0, np = 0;
+    __syncthreads();
+    while (i < i1 && nt < kTilesPerRound && np < p.pieces_per_round) {
+      const int32_t nb_s = (len_s + 15) >> 4;
+      const int32_t cnt = (int32_t)min((int64_t)min(nb_s - j, kTilesPerRound - nt), i1 - i);
+      if (cnt > 0) {
+        const bool fin = j + cnt == nb_s || i + cnt == i1;
+        if (!(cont && np == 0)) open_j0 = j;
+        if (lane == 0) {
+          Piece pc;
+          pc.s = s;
+          pc.g = g;
+          pc.j0 = j;
+          pc.kstart = nt;
+          pc.kend = nt + cnt;
+          pc.len = len_s;
+          pc.flags = (fin ? kFinal : 0) | (open_j0 == 0 && j + cnt == nb_s ? kWhole : 0) |
+                     (first ? kFirst : 0) | (cont && np == 0 ? kCont : 0);
+          pc.pad = 0;
+          pieces[np] = pc;
         }
-        __syncthreads();
-        auto block_of = [&](int32_t j) -> int64_t {
-          return __builtin_amdgcn_readfirstlane(s_ids[min(j, c1 - 1) - c0]);
-        };
-        Tile<DT, D> buf[DEPTH];
-        // Tiles are issued in order (the scheduler must not interleave
-        // them): the waits below count loads in issue order.
+        // Block ids of the piece and the query rows of heads g*G .. g*G+G-1
+        // (contiguous, at most 8 KiB): all loads of a 64-tile chunk are
+        // issued before anything is written, so one memory round trip
+        // stages them.
+        const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks + j;
+        const char* qsrc = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)s * p.num_q_heads + (int64_t)g * G) * Sh::kRow;
+        char* qdst = qlds + np * qbytes;
+        {
+          const int32_t b = lane < cnt ? trow[lane] : 0;
+          uint4 qc[8];
 #pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
-          const int64_t b = block_of(c0 + u);
-          load_tile<DT, D>(buf[u], kbase + b * block_stride, vbase + b * block_stride, k_off, v_off);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int32_t jb = c0; jb < c1; jb += DEPTH) {
+          for (int m = 0; m < 8; ++m) {
+            const int32_t o = (lane + 64 * m) * 16;
+            qc[m] = o < qbytes ? *reinterpret_cast<const uint4*>(qsrc + o) : uint4{0u, 0u, 0u, 0u};
+          }
+          if (lane < cnt) tiles[nt + lane] = ((uint32_t)b < (uint32_t)p.num_blocks ? b : 0) * p.num_kv_heads + g;
 #pragma unroll
-          for (int u = 0; u < DEPTH; ++u) {
-            const int32_t j = jb + u;
-            // Tiles past the end of the sub-piece (at most DEPTH-1) are
-            // fully masked: they leave m, l and o unchanged. Keeping the
-            // body free of branches keeps the compiler's wait counts exact.
-            const int32_t t0 = 16 * j;
-            const int32_t end = j < c1 ? min(t0 + 16, len_s) : t0;  // valid: [t0, end)
-            const int lim[1] = {end - 1};
-            attend_tile<DT, D, 1>(st, buf[u], qv, p.scale_log2, t0, lim, end, end < t0 + 16, kg);
-            // Always issue the next load (the last block again past the
-            // end) for the same reason.
-            const int64_t b = block_of(j + DEPTH);
-            load_tile<DT, D>(buf[u], kbase + b * block_stride, vbase + b * block_stride, k_off,
-                             v_off);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int m = 0; m < 8; ++m) {
+            const int32_t o = (lane + 64 * m) * 16;
+            if (o < qbytes) *reinterpret_cast<uint4*>(qdst + o) = qc[m];
           }
         }
+        for (int32_t t = 64 + lane; t < cnt; t += 64) {
+          const int32_t b = trow[t];
+          tiles[nt + t] = ((uint32_t)b < (uint32_t)p.num_blocks ? b : 0) * p.num_kv_heads + g;
+        }
+        ++np;
+        nt += cnt;
+        i += cnt;
+        j += cnt;
+        cont = !fin;
+        if (fin) first = false;
       }
-      if (j0 == 0 && j1 == nb_s) {
-        store_row<DT, D>(p.out, (int64_t)s * p.num_q_heads + g * p.group + n, st[0], kg,
-                         n < p.group);
-      } else {
-        write_partial<DT, D>(p, st[0], 2 * w + (first_piece ? 0 : 1), n, kg);
+      if (j >= nb_s) {  // next sequence, wrapping to the next head
+        j = 0;
+        if (++s == p.num_seqs) {
+          s = 0;
+          ++g;
+        }
+        if (i < i1) {
+          // lengths of the first 64 sequences are still in the scan registers
+          len_s = s < 64 ? __builtin_amdgcn_readlane(len0, s) : seq_len_uniform(p, s);
+        }
       }
-      i += j1 - j0;
-      first_piece = false;
     }
-    // Next sequence (wrapping to the next head).
-    if (i >= i1) break;
-    ++s;
-    if (s == p.num_seqs) {
-      s = 0;
-      ++g;
+    __syncthreads();
+
+    // ---- stream the round's tiles ---------------------------------------
+    int32_t pc = -1, kend = 0, j0 = 0, kstart = 0, plen = 0, pflags = 0, ps = 0, pg = 0;
+    auto tile_ptr = [&](int32_t k) -> int64_t {
+      return (int64_t)__builtin_amdgcn_readfirstlane(tiles[min(k, nt - 1)]) * Sh::kTileBytes;
+    };
+    // One tile: open the next piece at its first tile, attend, close the
+    // piece at its last tile.
+    auto step = [&](Tile<DT, D>& tl, int32_t k) {
+      if (k == kend) {
+        ++pc;
+        const Piece& P = pieces[pc];
+        ps = __builtin_amdgcn_readfirstlane(P.s);
+        pg = __builtin_amdgcn_readfirstlane(P.g);
+        j0 = __builtin_amdgcn_readfirstlane(P.j0);
+        kstart = __builtin_amdgcn_readfirstlane(P.kstart);
+        kend = __builtin_amdgcn_readfirstlane(P.kend);
+        plen = __builtin_amdgcn_readfirstlane(P.len);
+        pflags = __builtin_amdgcn_readfirstlane(P.flags);
+        if (!(pflags & kCont)) {
+          const char* qrow = qlds + pc * qbytes + n * Sh::kRow;
+#pragma unroll
+          for (int c = 0; c < Sh::kKLoads; ++c)
+            qv[0].c[c] = n < G ? *reinterpret_cast<const uint4*>(qrow + 64 * c + 16 * kg)
+                               : uint4{0u, 0u, 0u, 0u};
+          st[0].reset();
+        }
+      }
+      const int32_t t0 = 16 * (j0 + k - kstart);
+      const int32_t end = min(t0 + 16, plen);   // valid positions [t0, end)
+      const int lim[1] = {end - 1};
+      attend_tile<DT, D, 1>(st, tl, qv, p.scale_log2, t0, lim, end, end < t0 + 16, kg);
+      if (k == kend - 1 && (pflags & kFinal)) {
+        if (pflags & kWhole)
+          store_row<DT, D>(p.out, (int64_t)ps * p.num_q_heads + pg * G + n, st[0], kg, n < G);
+        else
+          write_partial<DT, D>(p, st[0], 2 * w + ((pflags & kFirst) ? 0 : 1), n, kg);
+      }
+    };
+    Tile<DT, D> buf[DEPTH];
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int64_t t = tile_ptr(u);
+      load_tile<DT, D>(buf[u], kpool + t, vpool + t, k_off, v_off);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    len_s = seq_len_uniform(p, s);
-    nb_s = (len_s + 15) >> 4;
-    j0 = 0;
+    int32_t kb = 0;
+    for (; kb + DEPTH <= nt; kb += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        step(buf[u], kb + u);
+        // the next load is always issued (the last tile again past the end)
+        const int64_t t = tile_ptr(kb + u + DEPTH);
+        load_tile<DT, D>(buf[u], kpool + t, vpool + t, k_off, v_off);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+      if (kb + u < nt) step(buf[u], kb + u);
   }
 }
 
@@ -393,23 +478,36 @@ int decode_depth() {
   return g_depth;
 }
 
+// Dynamic LDS of the split kernel: tile list, pieces, query rows.
 template <int DT, int D>
-hipError_t launch(const DecodeParams& prm, hipStream_t stream) {
+size_t split_lds_bytes(const DecodeParams& prm) {
+  return (size_t)kTilesPerRound * 4 + kPiecesPerRound * sizeof(Piece) +
+         (size_t)prm.pieces_per_round * prm.group * Shape<DT, D>::kRow;
+}
+
+template <int DT, int D>
+hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
+  const size_t lds = split_lds_bytes<DT, D>(prm);
+  if (phases & 1) {
   // 512-byte rows (fp32, head_dim 128) only fit two tiles in flight.
   const int depth = Shape<DT, D>::kRow > 256 ? 2 : decode_depth();
   if constexpr (Shape<DT, D>::kRow > 256) {
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
   } else if (depth == 2)
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
   else if (depth == 8)
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 8>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 8>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
   else
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 4>), dim3(prm.num_waves), dim3(64), 0, stream, prm);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(prm.num_seqs * prm.num_kv_heads), dim3(64),
-                     0, stream, prm);
-  return hipGetLastError();
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 4>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(prm.num_seqs * prm.num_kv_heads), dim3(64),
+                       0, stream, prm);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -449,7 +547,7 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return prefix + partial;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
   DecodeParams p;
   p.out = a.out;
   p.q = a.q;
@@ -468,10 +566,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.group = a.num_q_heads / a.num_kv_heads;
   p.num_waves = decode_num_waves();
   p.scale_log2 = a.scale * kLog2e;
-  if (a.dtype == PKV_BF16) {
-    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, stream) : launch<PKV_BF16, 64>(p, stream);
+  {
+    // query rows of up to 16 pieces per round, within 16 KiB of LDS
+    const int32_t qb = p.group * a.head_dim * (a.dtype == PKV_F32 ? 4 : 2);
+    int32_t k = 16384 / qb;
+    p.pieces_per_round = k < 2 ? 2 : (k > kPiecesPerRound ? kPiecesPerRound : k);
   }
-  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream) : launch<PKV_F32, 64>(p, stream);
+  if (a.dtype == PKV_BF16) {
+    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, phases, stream)
+                             : launch<PKV_BF16, 64>(p, phases, stream);
+  }
+  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, phases, stream)
+                           : launch<PKV_F32, 64>(p, phases, stream);
 }
 
 }  // namespace pkv

@@ -56,7 +56,8 @@ struct DecodeArgs {
 int decode_num_waves();
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.
+hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

@@ -265,3 +265,22 @@ def test_decode_full_size_sampled(name):
     kb = torch.from_numpy(blocks).cuda()
     assert to_numpy_storage(nat["k_cache"][kb]).tobytes() == ora["k_cache"][blocks].tobytes()
     assert to_numpy_storage(nat["v_cache"][kb]).tobytes() == ora["v_cache"][blocks].tobytes()
+
+
+def test_decode_phases_equal_whole_call():
+    """The split-KV kernel then the merge kernel, called apart, give exactly
+    the one-call result."""
+    _announce("decode phases")
+    w = workloads.custom("ph", 33, [3000, 17, 900, 2048, 5], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    nat = run_native(w, prefill=False)
+    dec = w.decode_seqs
+    q = torch.cat([w.seq_q(s) for s in dec]).cuda()
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(len(dec), 32, 8, 128)
+    args = (out, q, nat["k_cache"], nat["v_cache"], torch.from_numpy(nat["decode_table"]).cuda(),
+            torch.from_numpy(nat["decode_lens"]).cuda(), w.scale, ws)
+    pkv.decode(*args, phase="split")
+    pkv.decode(*args, phase="merge")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), nat["decode"].view(torch.int16))
