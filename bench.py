@@ -71,6 +71,50 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+class HipEvents:
+    """Timing events on the launch stream, created with
+    hipEventDisableSystemFence: recording them does not write back and
+    invalidate caches, so they time the commands between them without
+    perturbing them (the default events do both)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    DISABLE_TIMING = 0x2
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, timing=True):
+        e = self.ct.c_void_p()
+        flags = self.DISABLE_SYSTEM_FENCE | (0 if timing else self.DISABLE_TIMING)
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), flags)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        return e
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def sync(self, e):
+        self.lib.hipEventSynchronize(e)
+
+    def elapsed_us(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value * 1e3
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in DECODE_SRCS:
@@ -162,7 +206,8 @@ def main():
     n32 = S + S * maxb
     words = S + (n32 + 1) // 2
     pinned = [torch.empty(words, dtype=torch.int64).pin_memory() for _ in range(2)]
-    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    hip = HipEvents()
+    copied = [hip.create(timing=False), hip.create(timing=False)]
     d_stage = torch.empty(words, dtype=torch.int64, device=dev)
     d_slots = d_stage[:S]
     d_lens = d_stage[S:].view(torch.int32)[:S]
@@ -170,32 +215,33 @@ def main():
     pairs_buf = np.empty(2 * S, dtype=np.int64)
     kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
 
     total_steps = args.warmup + args.steps
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(total_steps)]
+    ev = [tuple(hip.create() for _ in range(4)) for _ in range(total_steps)]
     ctx_tokens = []
 
     def step(t):
         b = t % 2
         if t >= 2:
-            copied[b].synchronize()      # the copy that last read this staging buffer is done
+            hip.sync(copied[b])          # the copy that last read this staging buffer is done
         base = pinned[b].data_ptr()
         npairs = alloc.batch_append_into(sids, ones, base, pairs_buf)
         assert npairs == 0
         alloc.fill_block_table_into(sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
         ctx_tokens.append(int(pinned[b][S:].view(torch.int32)[:S].sum()))
         d_stage.copy_(pinned[b], non_blocking=True)
-        copied[b].record(stream)
+        hip.record(copied[b], sh)
         kc, vc = pools[t % len(pools)]
         e0, e1, e2, e3 = ev[t]
-        e0.record(stream)
+        hip.record(e0, sh)
         pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots)
-        e1.record(stream)
+        hip.record(e1, sh)
         # decode = split-KV kernel, then merge kernel (timed apart)
         pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="split")
-        e2.record(stream)
+        hip.record(e2, sh)
         pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="merge")
-        e3.record(stream)
+        hip.record(e3, sh)
 
     for t in range(args.warmup):
         step(t)
@@ -207,10 +253,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     timed = range(args.warmup, total_steps)
-    rc_us = np.array([ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in timed])
-    split_us = np.array([ev[t][1].elapsed_time(ev[t][2]) * 1e3 for t in timed])
-    merge_us = np.array([ev[t][2].elapsed_time(ev[t][3]) * 1e3 for t in timed])
-    dec_us = np.array([ev[t][1].elapsed_time(ev[t][3]) * 1e3 for t in timed])
+    rc_us = np.array([hip.elapsed_us(ev[t][0], ev[t][1]) for t in timed])
+    split_us = np.array([hip.elapsed_us(ev[t][1], ev[t][2]) for t in timed])
+    merge_us = np.array([hip.elapsed_us(ev[t][2], ev[t][3]) for t in timed])
+    dec_us = np.array([hip.elapsed_us(ev[t][1], ev[t][3]) for t in timed])
     kv_bytes = np.array([ctx_tokens[t] * kv_bytes_per_token for t in timed], dtype=np.float64)
     achieved = float(kv_bytes.mean() / (split_us.mean() * 1e-6) / 1e9)
     achieved_op = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
@@ -302,13 +348,15 @@ def prefill_leg(args, dev):
     for _ in range(5):
         pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax, w.scale)
     reps = max(10, args.steps // 2)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.create(), hip.create()
+    hip.record(e0, sh)
     for _ in range(reps):
         pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax, w.scale)
-    e1.record()
+    hip.record(e1, sh)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    us = hip.elapsed_us(e0, e1) / reps
     pairs = 0
     for spec in ch:
         # queries at positions cached .. total-1 see position+1 keys each
