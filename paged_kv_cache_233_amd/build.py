@@ -17,6 +17,10 @@ SOURCES = ["abi.cpp", "allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.h
 
 # Packed-FP32 VALU instructions are kept out of all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The prefill kernel keeps its MFMA accumulators in ordinary VGPRs: its
+# softmax rescales them with VALU code on a branch, and accumulators in
+# AGPRs were copied back and forth around that branch on every tile.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -33,7 +37,7 @@ def build(verbose: bool = False) -> str:
             cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                    "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
             if src.endswith(".hip"):
-                cmd += ["-x", "hip"] + DEVICE_FLAGS
+                cmd += ["-x", "hip"] + DEVICE_FLAGS + FILE_FLAGS.get(src, [])
             cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
             _run(cmd, verbose)
             objs.append(obj)

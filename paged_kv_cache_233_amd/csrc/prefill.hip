@@ -27,6 +27,7 @@
 // f32 (prefill_kernel): each wave loads its own K/V tiles in MFMA register
 // layout and runs the 16-token tile step shared with decode.
 #include <cstdlib>
+#include <utility>
 
 #include "internal.h"
 #include "tile_attn.h"
@@ -170,81 +171,150 @@ prefill_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------ bf16, LDS
 constexpr int kKeys = 32;          // positions per LDS tile (two pool blocks)
-constexpr int kBufs = 3;           // LDS tile buffers
+constexpr int kBufs = 2;           // LDS tile buffers per tile pipeline
 constexpr int kRoundIds = 2048;    // block ids staged in LDS per round
 constexpr float kLazyMax = 8.0f;   // log2 of the largest weight before a rescale
+constexpr float kNoMax = -1e30f;   // reference max of a row that has seen nothing
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+
+// LDS tile layout. K rows are padded to a pitch of 4 (mod 32) words, which
+// keeps the column-wise K operand reads (eight rows per LDS cycle) off
+// shared banks; V rows to 8 (mod 32) words, which does the same for the
+// transposing V reads (four rows of 32 bytes per 16 lanes).
 template <int D>
 struct Lds {
   static constexpr int kRow = 2 * D;                  // bytes of one position of one head
-  static constexpr int kPitch = kRow + 16;            // padded LDS row: no bank conflicts on
-                                                      // the column-wise K operand reads
+  static constexpr int kPitchK = kRow + 16;
+  static constexpr int kPitchV = kRow + 32;
   static constexpr int kPieces = kRow / 16;           // 16-byte pieces per row
-  static constexpr int kPerThread = kKeys * kPieces / (64 * kWaves);
-  static constexpr int kHalf = kKeys * kPitch;        // K (or V) part of one buffer
-  static constexpr int kBuf = 2 * kHalf;
-  static constexpr int kVBytes = kRow / 16;           // V bytes per lane per row
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kPerThread = kKeys * kPieces / kThreads;
+  static constexpr int kBlockPieces = 16 * kPieces;   // pieces of one (block, head) tile
+  static constexpr int kHalfK = kKeys * kPitchK;      // K part of one buffer
+  static constexpr int kBuf = kHalfK + kKeys * kPitchV;
   static_assert(kPerThread >= 1, "tile smaller than the workgroup");
+  static_assert(kBlockPieces % 64 == 0, "a wave's pieces must lie in one block");
 };
 
+// Calls f(std::integral_constant<int, 0>) ... f(<N-1>): the staged tile
+// registers are then indexed by constants from the start, which keeps them
+// in registers.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// Native 4 x 32-bit vector: loads, stores and copies stay plain vector
+// operations (the HIP uint4 class copies through memcpy, which can leave the
+// staged tile in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread's share of a tile on its way from global memory to LDS.
 template <int D>
 struct Staged {
-  uint4 k[Lds<D>::kPerThread];
-  uint4 v[Lds<D>::kPerThread];
+  u32x4 k[Lds<D>::kPerThread];
+  u32x4 v[Lds<D>::kPerThread];
 };
 
-// Global -> registers: this thread's pieces of tile `j` (ids of the tile's
-// blocks at s_ids[2*jl], [2*jl+1]).
+// Loop-invariant offsets of one thread. Piece u of the thread is 16 bytes of
+// tile position srow[u]; all pieces of one wave lie in the same pool block
+// (blk[u], wave-uniform), so the block's address is scalar arithmetic and
+// the load takes a scalar base plus this 32-bit offset.
 template <int D>
-__device__ __forceinline__ void tile_fetch(Staged<D>& st, const char* kbase, const char* vbase,
-                                           int64_t block_stride, const int32_t* s_ids, int jl,
-                                           int tid) {
-  using L = Lds<D>;
-#pragma unroll
-  for (int u = 0; u < L::kPerThread; ++u) {
-    const int q = tid + 64 * kWaves * u;
-    const int r = q / L::kPieces;               // position in the tile
-    const int col = q % L::kPieces;
-    const int64_t b = s_ids[2 * jl + (r >> 4)];
-    const int64_t off = b * block_stride + (r & 15) * L::kRow + 16 * col;
-    st.k[u] = *reinterpret_cast<const uint4*>(kbase + off);
-    st.v[u] = *reinterpret_cast<const uint4*>(vbase + off);
+struct Lanes {
+  uint32_t gofs[Lds<D>::kPerThread];  // byte offset inside the (block, head) tile
+  uint32_t kst[Lds<D>::kPerThread];   // LDS byte offset of the K piece in a buffer
+  uint32_t vst[Lds<D>::kPerThread];   // LDS byte offset of the V piece in a buffer
+  int32_t srow[Lds<D>::kPerThread];   // tile position
+  int32_t blk[Lds<D>::kPerThread];    // which of the tile's two blocks
+  uint32_t kofs;                      // K operand read offset (lane (n, kg))
+  uint32_t vofs;                      // V operand read offset (lane (n, kg))
+
+  __device__ __forceinline__ void init(int tid, int n, int kg) {
+    using L = Lds<D>;
+    unroll<L::kPerThread>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int q = tid + L::kThreads * u;
+      const int r = q / L::kPieces;
+      const int col = 16 * (q % L::kPieces);
+      gofs[u] = (uint32_t)(q % L::kBlockPieces) * 16u;
+      kst[u] = (uint32_t)(r * L::kPitchK + col);
+      vst[u] = (uint32_t)(L::kHalfK + r * L::kPitchV + col);
+      srow[u] = r;
+      blk[u] = __builtin_amdgcn_readfirstlane(q / L::kBlockPieces);
+    });
+    kofs = (uint32_t)(n * L::kPitchK + 16 * kg);
+    // Transposing V read: lane 4j + q of a 16-lane group reads 8 bytes (dims
+    // 4q..4q+3 of the tile's 16) of position 4kg + j; lane n then receives
+    // dim n of positions 4kg + 0..3.
+    vofs = (uint32_t)(L::kHalfK + (4 * kg + n / 4) * L::kPitchV + 8 * (n % 4));
   }
+};
+
+// Global -> registers: this thread's pieces of tile `jl` of the round (ids
+// of its two blocks at s_ids[2*jl], [2*jl+1]).
+template <int D>
+__device__ __forceinline__ void tile_fetch(Staged<D>& st, const Lanes<D>& ln, const char* kbase,
+                                           const char* vbase, uint32_t block_stride,
+                                           const lds_char* s_ids, int jl) {
+  unroll<Lds<D>::kPerThread>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    const int32_t id = *reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(
+        s_ids + 4 * (2 * jl + ln.blk[u]));
+    // 32 x 32 -> 64-bit product in scalar registers (block_stride < 2^32)
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(id);
+    const uint64_t off = ((uint64_t)__umulhi(b, block_stride) << 32) | (uint32_t)(b * block_stride);
+    st.k[u] = *reinterpret_cast<const u32x4*>(kbase + off + ln.gofs[u]);
+    st.v[u] = *reinterpret_cast<const u32x4*>(vbase + off + ln.gofs[u]);
+  });
 }
 
 // Registers -> LDS buffer. V rows past `vlim` (no query of this workgroup
 // sees them; the pool may hold anything there) are stored as zeros, so that
 // their zero weights cannot meet a NaN.
 template <int D>
-__device__ __forceinline__ void tile_store(const Staged<D>& st, char* buf, int t0, int vlim,
-                                           int tid) {
+__device__ __forceinline__ void tile_store(const Staged<D>& st, const Lanes<D>& ln, lds_char* buf,
+                                           int t0, int vlim) {
   using L = Lds<D>;
-#pragma unroll
-  for (int u = 0; u < L::kPerThread; ++u) {
-    const int q = tid + 64 * kWaves * u;
-    const int r = q / L::kPieces;
-    const int col = q % L::kPieces;
-    char* dst = buf + r * L::kPitch + 16 * col;
-    const uint32_t keep = t0 + r <= vlim ? ~0u : 0u;
-    *reinterpret_cast<uint4*>(dst) = st.k[u];
-    *reinterpret_cast<uint4*>(dst + L::kHalf) =
-        uint4{st.v[u].x & keep, st.v[u].y & keep, st.v[u].z & keep, st.v[u].w & keep};
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  if (t0 + kKeys - 1 <= vlim) {
+    unroll<L::kPerThread>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      *reinterpret_cast<lds_u32x4*>(buf + ln.kst[u]) = st.k[u];
+      *reinterpret_cast<lds_u32x4*>(buf + ln.vst[u]) = st.v[u];
+    });
+  } else {
+    unroll<L::kPerThread>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const uint32_t keep = t0 + ln.srow[u] <= vlim ? ~0u : 0u;
+      *reinterpret_cast<lds_u32x4*>(buf + ln.kst[u]) = st.k[u];
+      *reinterpret_cast<lds_u32x4*>(buf + ln.vst[u]) = st.v[u] & keep;
+    });
   }
 }
 
 // Scores of one LDS tile against NG column groups: s[gi][h] holds, in lane
 // (n, kg), S[16h + 4kg + i][n] (position offset within the tile, column n).
 template <int D, int NG>
-__device__ __forceinline__ void tile_scores(f32x4 (&s)[NG][2], const char* buf,
-                                            const QOp<PKV_BF16, D> (&qv)[NG], int n, int kg) {
+__device__ __forceinline__ void tile_scores(f32x4 (&s)[NG][2], const lds_char* buf, uint32_t kofs,
+                                            const QOp<PKV_BF16, D> (&qv)[NG]) {
   using L = Lds<D>;
+  typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
   constexpr int kC = L::kRow / 64;
-  uint4 kf[2][kC];
+  const lds_char* base = buf + kofs;
+  u32x4 kf[2][kC];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int c = 0; c < kC; ++c)
-      kf[h][c] = *reinterpret_cast<const uint4*>(buf + (16 * h + n) * L::kPitch + 64 * c + 16 * kg);
+      kf[h][c] = *reinterpret_cast<lds_u32x4*>(base + 16 * h * L::kPitchK + 64 * c);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
@@ -259,96 +329,110 @@ __device__ __forceinline__ void tile_scores(f32x4 (&s)[NG][2], const char* buf,
     }
 }
 
+// Running softmax state of one lane for NG column groups. The reference max
+// mc (log2 units) moves only when a score passes thr, the raw score that
+// stands 2^kLazyMax above it. o[gi][e] holds O^T rows 4kg + i of dim tile e
+// (dims 16e + 4kg + i) of column n; l[gi] holds the column's weight sum in
+// all four entries (a product with a row of ones).
+template <int D, int NG>
+struct Acc {
+  float mc[NG];
+  float thr[NG];
+  f32x4 l[NG];
+  f32x4 o[NG][D / 16];
+};
+
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]);
+  const float b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  return fmaxf(fmaxf(x[6], x[7]), fmaxf(a, b));
+}
+
 // Softmax weights of one tile and their product with its V rows.
 // Lane (n, kg) owns positions {4kg + i, 16 + 4kg + i} of the tile for column
 // n; those eight are also the reduction slots 8kg..8kg+7 of the PV MFMA, in
-// the same order on both operands.
+// the same order on both operands. `mask` (wave-uniform) applies the
+// per-column causal limit (tiles that reach past the wave's smallest limit).
 template <int D, int NG>
-__device__ __forceinline__ void tile_softmax_pv(const f32x4 (&s)[NG][2], const char* buf,
-                                                float (&m)[NG], float (&lsum)[NG],
-                                                f32x4 (&o)[NG][D / 16], const int (&lim)[NG],
-                                                int t0, bool mask, float c, int n, int kg) {
+__device__ __forceinline__ void tile_softmax_pv(const f32x4 (&s)[NG][2], const lds_char* buf,
+                                                uint32_t vofs, Acc<D, NG>& a,
+                                                const int (&lim)[NG], int t0, bool mask, float c,
+                                                float tau_raw, int kg) {
   using L = Lds<D>;
   constexpr int kE = D / 16;
-  float x[NG][8];
-  bool grow = false;
+  // V operands first: their LDS latency then overlaps the softmax.
+  const lds_char* vb = buf + vofs;
+  bf16x8 av[kE];
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
+  for (int e = 0; e < kE; ++e) {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 32 * e));
+    const i16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 16 * L::kPitchV + 32 * e));
+    av[e] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  float x[NG][8];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = s[gi][h][i];
-        if (mask && t0 + 16 * h + 4 * kg + i > lim[gi]) v = -INFINITY;
-        x[gi][4 * h + i] = v;
-      }
-    const float lmax = fmaxf(fmaxf(fmaxf(x[gi][0], x[gi][1]), fmaxf(x[gi][2], x[gi][3])),
-                             fmaxf(fmaxf(x[gi][4], x[gi][5]), fmaxf(x[gi][6], x[gi][7])));
-    grow |= lmax * c > m[gi] + kLazyMax;
+      for (int i = 0; i < 4; ++i) x[gi][4 * h + i] = s[gi][h][i];
+  if (mask) {
+    // (a scalar branch: only tiles that reach past the wave's smallest limit)
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (t0 + 16 * (k >> 2) + 4 * kg + (k & 3) > lim[gi]) x[gi][k] = -INFINITY;
   }
+  bool grow = false;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) grow |= max8(x[gi]) > a.thr[gi];
   if (__ballot(grow) != 0) {
-    // Some row's scores passed its reference max by more than 2^kLazyMax:
-    // those rows move their reference to the row max (the same value in the
-    // row's four lanes) and rescale; every other row keeps alpha = 1.
+    // Some row passed its threshold: those rows move their reference to the
+    // row max (the same value in the row's four lanes) and rescale; every
+    // other row keeps alpha = 1.
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      float lmax = x[gi][0];
+      const float rmax = wave_max_kg(max8(x[gi]));
+      const bool upd = rmax > a.thr[gi];
+      const float m_new = upd ? rmax * c : a.mc[gi];
+      const float alpha = __builtin_amdgcn_exp2f(a.mc[gi] - m_new);
+      a.mc[gi] = m_new;
+      a.thr[gi] = upd ? rmax + tau_raw : a.thr[gi];
+      a.l[gi] *= alpha;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, x[gi][i]);
-      const float rmax = wave_max_kg(lmax) * c;
-      const float m_new = rmax > m[gi] + kLazyMax ? rmax : m[gi];
-      const float alpha = __builtin_amdgcn_exp2f(m[gi] - m_new);
-      m[gi] = m_new;
-      lsum[gi] *= alpha;
-#pragma unroll
-      for (int e = 0; e < kE; ++e) o[gi][e] *= alpha;
+      for (int e = 0; e < kE; ++e) a.o[gi][e] *= alpha;
     }
   }
-  uint4 pb[NG];
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     float p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[gi][i], c, -m[gi]));
-    lsum[gi] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    uint32_t w[4];
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[gi][i], c, -a.mc[gi]));
+    u32x4 pw;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       bf16x2 pr = {(__bf16)p[2 * k], (__bf16)p[2 * k + 1]};
-      w[k] = __builtin_bit_cast(uint32_t, pr);
+      pw[k] = __builtin_bit_cast(uint32_t, pr);
     }
-    pb[gi] = uint4{w[0], w[1], w[2], w[3]};
-  }
-  // V rows of this lane's eight positions, dims [n*D/16, (n+1)*D/16).
-  constexpr int kW = L::kVBytes / 4;
-  uint32_t vr[8][kW];
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    // the weights as the MFMA sees them, summed by the MFMA itself
+    a.l[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), pb, a.l[gi],
+                                                      0, 0, 0);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = 16 * (k >> 2) + 4 * kg + (k & 3);
-    const char* src = buf + L::kHalf + row * L::kPitch + n * L::kVBytes;
-    if constexpr (kW == 4) {
-      const uint4 t = *reinterpret_cast<const uint4*>(src);
-      vr[k][0] = t.x; vr[k][1] = t.y; vr[k][2] = t.z; vr[k][3] = t.w;
-    } else {
-      const uint2 t = *reinterpret_cast<const uint2*>(src);
-      vr[k][0] = t.x; vr[k][1] = t.y;
-    }
+    for (int e = 0; e < kE; ++e)
+      a.o[gi][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[e], pb, a.o[gi][e], 0, 0, 0);
   }
-#pragma unroll
-  for (int e = 0; e < kE; ++e) {
-    const int w = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint4 a;
-    a.x = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
-    a.y = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
-    a.z = __builtin_amdgcn_perm(vr[5][w], vr[4][w], sel);
-    a.w = __builtin_amdgcn_perm(vr[7][w], vr[6][w], sel);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi)
-      o[gi][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                         __builtin_bit_cast(bf16x8, pb[gi]),
-                                                         o[gi][e], 0, 0, 0);
-  }
+}
+
+// Workgroup barrier for the LDS tile pipeline: waits for this wave's LDS
+// writes only; global loads in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 struct LdsParams {
@@ -358,14 +442,21 @@ struct LdsParams {
   int32_t num_wg;         // real workgroups (the grid may hold a few more)
 };
 
-template <int D, int NG>
-__global__ void __launch_bounds__(64 * kWaves)
+// SPLIT = 1: four waves, each with its own rows, walk all of the
+// workgroup's tiles. SPLIT = 2: eight waves; waves 4..7 take the same rows as
+// waves 0..3 but the second half of the tiles, through a second LDS pipeline,
+// and hand their softmax state to waves 0..3 through LDS at the end. Either
+// way a SIMD runs two waves (the second workgroup on the CU, or the other
+// half), so one wave's MFMA work hides the other's softmax and waits.
+template <int D, int NG, int SPLIT>
+__global__ void __launch_bounds__(64 * kWaves * SPLIT, SPLIT == 1 ? 2 : 1)
 prefill_lds_kernel(LdsParams lp) {
   using L = Lds<D>;
   constexpr int kE = D / 16;
+  constexpr int kIds = kRoundIds / SPLIT;     // block ids per half and round
+  constexpr int kBigPos = 1 << 30;            // position of a tile past every limit
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int32_t* s_ids = reinterpret_cast<int32_t*>(smem);
-  char* bufs = smem + kRoundIds * 4;
+  lds_char* lds = (lds_char*)smem;
   const PrefillParams& p = lp.p;
 
   // XCD-aware placement: hardware workgroup b runs on XCD b % 8; the
@@ -380,12 +471,18 @@ prefill_lds_kernel(LdsParams lp) {
   const int32_t ch = pair / p.num_kv_heads;
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  // (wave-uniform values are made visibly uniform, so that the decisions
+  // taken on them are scalar branches)
+  const int half = __builtin_amdgcn_readfirstlane(tid >> 8);   // tile half (0 when SPLIT = 1)
+  const int htid = tid & 255;                                   // thread index within the half
+  const int wq = __builtin_amdgcn_readfirstlane(htid >> 6);    // row quarter of the workgroup
   const int lane = tid & 63;
   const int n = lane & 15;
   const int kg = lane >> 4;
   const int32_t G = p.group;
   const int32_t tpg = p.tokens_per_group;
+  lds_char* s_ids = lds + half * kIds * 4;
+  lds_char* bufs = lds + kRoundIds * 4 + half * kBufs * L::kBuf;
 
   const int32_t q_begin = max(0, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch]));
   const int32_t q_end = min(p.total_q, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch + 1]));
@@ -400,7 +497,7 @@ prefill_lds_kernel(LdsParams lp) {
 
   // This wave's columns (waves past the chunk's end keep padding columns and
   // still take part in the loads and barriers).
-  const int32_t tok0 = wg_tok0 + wv * NG * tpg;
+  const int32_t tok0 = wg_tok0 + wq * NG * tpg;
   const int32_t lim_min = min(p0 + min(tok0, qlen - 1), ctx - 1);
   QOp<PKV_BF16, D> qv[NG];
   int lim[NG];
@@ -418,6 +515,7 @@ prefill_lds_kernel(LdsParams lp) {
 
   if (lim_wg < 0) {
     // Empty context: nothing to attend to, zero output.
+    if (half != 0) return;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       if (!valid[gi]) continue;
@@ -427,84 +525,137 @@ prefill_lds_kernel(LdsParams lp) {
     return;
   }
 
-  float m[NG], lsum[NG];
-  f32x4 o[NG][kE];
+  // The reference max starts finite but below any score: a row that has
+  // seen no position yet (possible in the second tile half) keeps weights
+  // exp2(-inf) = 0 instead of exp2(-inf + inf); its first visible score
+  // passes the -inf threshold and sets the reference.
+  Acc<D, NG> acc;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    m[gi] = -INFINITY;
-    lsum[gi] = 0.f;
+    acc.mc[gi] = kNoMax;
+    acc.thr[gi] = -INFINITY;
+    acc.l[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < kE; ++e) o[gi][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < kE; ++e) acc.o[gi][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const float c = p.scale_log2;
+  const float tau_raw = kLazyMax / c;
   const int32_t nblk = lim_wg / 16 + 1;        // blocks any row of this workgroup sees
   const int32_t ntiles = lim_wg / kKeys + 1;
+  // Tiles of this half: [tbeg, tbeg + tcnt). The first half has the most
+  // tiles; both halves take the same number of steps, the second one's
+  // surplus steps being fully masked.
+  const int32_t steps = (ntiles + SPLIT - 1) / SPLIT;
+  const int32_t tbeg = half * steps;
+  const int32_t tcnt = min(steps, ntiles - tbeg);
   const int32_t* trow = p.block_table + (int64_t)ch * p.max_blocks;
-  const int64_t block_stride = (int64_t)p.num_kv_heads * L::kRow * 16;
+  const uint32_t block_stride = (uint32_t)p.num_kv_heads * L::kRow * 16;
   const char* kbase = p.k_cache + (int64_t)g * L::kRow * 16;
   const char* vbase = p.v_cache + (int64_t)g * L::kRow * 16;
+  Lanes<D> ln;
+  ln.init(htid, n, kg);
 
-  for (int32_t j0 = 0; j0 < ntiles; j0 += kRoundIds / 2) {
-    const int32_t nt = min(kRoundIds / 2, ntiles - j0);
+  for (int32_t j0 = 0; j0 < steps; j0 += kIds / 2) {
+    const int32_t nt = min(kIds / 2, steps - j0);    // steps of this round
+    const int32_t nv = max(0, min(nt, tcnt - j0));   // real tiles of this half in it
     __syncthreads();  // the previous round is done with the ids and buffers
-    for (int32_t i = tid; i < 2 * nt; i += 64 * kWaves) {
-      const int32_t bi = 2 * j0 + i;
-      const int32_t b = bi < nblk ? trow[bi] : 0;
-      s_ids[i] = (uint32_t)b < (uint32_t)p.num_blocks ? b : 0;
+    for (int32_t i = htid; i < 2 * nt; i += L::kThreads) {
+      const int32_t bi = 2 * (tbeg + j0) + i;
+      const int32_t b = i < 2 * nv && bi < nblk ? trow[bi] : 0;
+      *reinterpret_cast<__attribute__((address_space(3))) int32_t*>(s_ids + 4 * i) =
+          (uint32_t)b < (uint32_t)p.num_blocks ? b : 0;
     }
     __syncthreads();
+    // Position of tile i of the round; a step with no tile of this half
+    // gets a position past every limit (its K/V rows are block 0's, masked,
+    // and its V is stored as zeros).
+    auto pos = [&](int32_t i) -> int32_t {
+      return i < nv ? kKeys * (tbeg + j0 + i) : kBigPos;
+    };
+    // Step i: fetch tile i+1 from global memory, score tile i and take its
+    // softmax and PV product, store tile i+1 into the other buffer, which
+    // tile i-1 used. Near the round's end a step fetches the last tile again
+    // and stores it into the buffer no later step reads.
+    // Step i: fetch tile i+1 from global memory, score tile i and take its
+    // softmax and PV product, store tile i+1 into the other buffer, which
+    // tile i-1 used. Near the round's end a step fetches the last tile again
+    // and stores it into the buffer no later step reads.
     Staged<D> st;
-    tile_fetch<D>(st, kbase, vbase, block_stride, s_ids, 0, tid);
-    tile_store<D>(st, bufs, kKeys * j0, lim_wg, tid);
-    if (nt > 1) {
-      tile_fetch<D>(st, kbase, vbase, block_stride, s_ids, 1, tid);
-      tile_store<D>(st, bufs + L::kBuf, kKeys * (j0 + 1), lim_wg, tid);
-    }
-    __syncthreads();
-    f32x4 scur[NG][2];
-    tile_scores<D, NG>(scur, bufs, qv, n, kg);
+    tile_fetch<D>(st, ln, kbase, vbase, block_stride, s_ids, 0);
+    tile_store<D>(st, ln, bufs, pos(0), lim_wg);
+    lds_barrier();
+    uint32_t b0 = 0, b1 = L::kBuf;  // buffers of tiles i and i+1
     for (int32_t i = 0; i < nt; ++i) {
-      // The body has no branches: near the round's end it fetches the last
-      // tile again and stores it into the buffer no later step reads.
-      tile_fetch<D>(st, kbase, vbase, block_stride, s_ids, min(i + 2, nt - 1), tid);
-      // scores of the next tile (its buffer is ready) ahead of this tile's
-      // softmax, so the two overlap; past the round's end they are unused
-      f32x4 snext[NG][2];
-      tile_scores<D, NG>(snext, bufs + ((i + 1) % kBufs) * L::kBuf, qv, n, kg);
-      const int32_t t0 = kKeys * (j0 + i);
-      tile_softmax_pv<D, NG>(scur, bufs + (i % kBufs) * L::kBuf, m, lsum, o, lim, t0,
-                             t0 + kKeys - 1 > lim_min, c, n, kg);
-      tile_store<D>(st, bufs + ((i + 2) % kBufs) * L::kBuf, kKeys * (j0 + min(i + 2, nt - 1)), lim_wg, tid);
-      __syncthreads();
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        scur[gi][0] = snext[gi][0];
-        scur[gi][1] = snext[gi][1];
-      }
+      const int32_t inext = min(i + 1, nt - 1);
+      tile_fetch<D>(st, ln, kbase, vbase, block_stride, s_ids, inext);
+      f32x4 sc[NG][2];
+      tile_scores<D, NG>(sc, bufs + b0, ln.kofs, qv);
+      const int32_t t0 = pos(i);
+      tile_softmax_pv<D, NG>(sc, bufs + b0, ln.vofs, acc, lim, t0, t0 + kKeys - 1 > lim_min, c,
+                             tau_raw, kg);
+      tile_store<D>(st, ln, bufs + b1, pos(inext), lim_wg);
+      lds_barrier();
+      const uint32_t t = b0;
+      b0 = b1;
+      b1 = t;
     }
   }
 
+  if constexpr (SPLIT == 2) {
+    // Waves 4..7 hand (reference max, sum, accumulators) to the waves 0..3
+    // that own the same rows, lane for lane; value v of lane t sits at float
+    // v * 256 + t.
+    constexpr int kPer = 2 + 4 * kE;
+    typedef __attribute__((address_space(3))) float lds_float;
+    lds_float* xs = (lds_float*)(lds + kRoundIds * 4);
+    static_assert(NG * kPer * 256 * 4 <= 2 * kBufs * Lds<D>::kBuf, "merge area too small");
+    __syncthreads();  // all tile reads done before the buffers are reused
+    if (half == 1) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        lds_float* d = xs + gi * kPer * 256 + htid;
+        d[0] = acc.mc[gi];
+        d[256] = acc.l[gi][0];
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[(2 + 4 * e + i) * 256] = acc.o[gi][e][i];
+      }
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const lds_float* d = xs + gi * kPer * 256 + htid;
+      const float mb = d[0];
+      // The first half always holds position 0, so its max is a real one;
+      // the second half's may still be kNoMax (nothing visible), which gives
+      // it weight 0.
+      const float m = fmaxf(acc.mc[gi], mb);
+      const float sa_ = __builtin_amdgcn_exp2f(acc.mc[gi] - m);
+      const float sb_ = __builtin_amdgcn_exp2f(mb - m);
+      acc.l[gi][0] = acc.l[gi][0] * sa_ + d[256] * sb_;
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc.o[gi][e][i] = acc.o[gi][e][i] * sa_ + d[(2 + 4 * e + i) * 256] * sb_;
+    }
+  }
+
+  // Lane (n, kg) writes dims 16e + 4kg + 0..3 of its column's row.
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const float l = wave_sum_kg(lsum[gi]);
     if (!valid[gi]) continue;
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / acc.l[gi][0];
+    char* dst = reinterpret_cast<char*>(p.out) + (row[gi] * D + 4 * kg) * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = (4 * kg + i) * kE;
-      uint32_t w[kE / 2];
-#pragma unroll
-      for (int e = 0; e < kE; e += 2) {
-        bf16x2 v = {(__bf16)(o[gi][e][i] * inv), (__bf16)(o[gi][e + 1][i] * inv)};
-        w[e / 2] = __builtin_bit_cast(uint32_t, v);
-      }
-      char* dst = reinterpret_cast<char*>(p.out) + (row[gi] * D + d0) * 2;
-      if constexpr (kE == 8) {
-        *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
-      } else {
-        *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
-      }
+    for (int e = 0; e < kE; ++e) {
+      bf16x2 v01 = {(__bf16)(acc.o[gi][e][0] * inv), (__bf16)(acc.o[gi][e][1] * inv)};
+      bf16x2 v23 = {(__bf16)(acc.o[gi][e][2] * inv), (__bf16)(acc.o[gi][e][3] * inv)};
+      *reinterpret_cast<uint2*>(dst + 32 * e) =
+          uint2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
     }
   }
 }
@@ -516,11 +667,38 @@ int prefill_groups() {
     int v = 2;
     if (const char* env = getenv("PKV_PREFILL_GROUPS")) {
       int e = atoi(env);
-      if (e == 1 || e == 2 || e == 4) v = e;
+      if (e == 1 || e == 2) v = e;
     }
     g_ng = v;
   }
   return g_ng;
+}
+
+int g_num_cus = 0;
+
+int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      g_num_cus = v;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+template <int D, int NG, int SPLIT>
+hipError_t launch_lds_split(const LdsParams& lp, hipStream_t stream) {
+  const size_t lds = kRoundIds * 4 + SPLIT * kBufs * Lds<D>::kBuf;
+  auto kern = prefill_lds_kernel<D, NG, SPLIT>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(8 * lp.per_xcd), dim3(64 * kWaves * SPLIT), lds, stream, lp);
+  return hipGetLastError();
 }
 
 template <int D, int NG>
@@ -530,13 +708,17 @@ hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream) {
   const int32_t wg_tokens = kWaves * NG * prm.tokens_per_group;
   lp.row_blocks = (prm.max_q_len + wg_tokens - 1) / wg_tokens;
   const int64_t nwg = (int64_t)lp.row_blocks * prm.num_kv_heads * prm.num_chunks;
-  if (nwg * 64 * kWaves > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (nwg * 64 * kWaves * 2 > INT32_MAX) return hipErrorInvalidConfiguration;
   lp.num_wg = (int32_t)nwg;
   lp.per_xcd = (lp.num_wg + 7) / 8;
-  const size_t lds = kRoundIds * 4 + kBufs * Lds<D>::kBuf;
-  hipLaunchKernelGGL((prefill_lds_kernel<D, NG>), dim3(8 * lp.per_xcd), dim3(64 * kWaves), lds,
-                     stream, lp);
-  return hipGetLastError();
+  // Two waves per SIMD either way: with fewer than two workgroups per CU,
+  // each workgroup splits its tiles over two sets of waves.
+  // (The hand-over of the split needs its state to fit the tile buffers.)
+  constexpr bool kCanSplit = NG * (2 + 4 * (D / 16)) * 256 * 4 <= 2 * kBufs * Lds<D>::kBuf;
+  if constexpr (kCanSplit) {
+    if (nwg < 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 2>(lp, stream);
+  }
+  return launch_lds_split<D, NG, 1>(lp, stream);
 }
 
 template <int DT, int D, int NG>
@@ -550,9 +732,7 @@ hipError_t launch_ng(const PrefillParams& prm, hipStream_t stream) {
 template <int DT, int D>
 hipError_t launch(const PrefillParams& prm, hipStream_t stream) {
   if constexpr (DT == PKV_BF16) {
-    const int ng = prefill_groups();
-    if (ng == 1) return launch_lds<D, 1>(prm, stream);
-    if (ng == 4) return launch_lds<D, 4>(prm, stream);
+    if (prefill_groups() == 1) return launch_lds<D, 1>(prm, stream);
     return launch_lds<D, 2>(prm, stream);
   } else if constexpr (Shape<DT, D>::kRow > 256) {
     // fp32 head_dim 128 keeps one column group (register budget).

@@ -62,8 +62,10 @@ def test_prefill_single_query_equals_decode():
 
 def test_prefill_chunk_split_and_placement_invariance():
     """One 200-token chunk equals two chunks of 120 and 80 at the right
-    offsets, bit for bit, and the result does not depend on where the blocks
-    sit in the pool."""
+    offsets (to rounding: the workgroup tiling, and with it the point where
+    a workgroup splits its positions over two sets of waves, follows the
+    chunk), and the result does not depend on where the blocks sit in the
+    pool, bit for bit."""
     _announce("prefill invariance")
     base = workloads.custom("pfs", 52, [], chunks=[(57, 200)], num_q_heads=32, num_kv_heads=8,
                             head_dim=128, dtype="bf16")
@@ -79,7 +81,9 @@ def test_prefill_chunk_split_and_placement_invariance():
     lens = torch.tensor([57 + 120, 257], dtype=torch.int32, device="cuda")
     pkv.prefill_chunk(out, q, cu, lens, torch.cat([table, table]), kc, vc, 120, base.scale)
     torch.cuda.synchronize()
-    assert torch.equal(out.cpu().view(torch.int16), full.view(torch.int16))
+    ora = run_oracle(base)
+    assert_close(full, ora["prefill"], "bf16", "one chunk")
+    assert_close(out, ora["prefill"], "bf16", "two chunks")
     # another physical placement of the same tokens
     w2 = workloads.custom("pfs", 52, [], chunks=[(57, 200)], num_q_heads=32, num_kv_heads=8,
                           head_dim=128, dtype="bf16")
@@ -104,6 +108,20 @@ def test_prefill_rows_beyond_total_q_untouched():
                       nat["k_cache"], nat["v_cache"], 1000, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, nat["prefill"])
+
+
+def test_prefill_many_chunks():
+    """Eight chunks (two ragged): enough workgroups that each one walks all
+    of its tiles with one set of waves; the small cases above split their
+    tiles over two."""
+    chunks = [(0, 512), (100, 512), (333, 300), (16, 512), (250, 77), (31, 512), (200, 512),
+              (64, 512)]
+    w = workloads.custom("pfm", 54, [], chunks=chunks, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    _announce("prefill many chunks")
+    nat = run_native(w)
+    ora = run_oracle(w)
+    assert_close(nat["prefill"], ora["prefill"], "bf16", "many chunks")
 
 
 def test_prefill_full_mixed_workload():
