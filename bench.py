@@ -2,11 +2,12 @@
 
 One step = one decode step of one attention layer for the whole batch:
   host   append one token to every sequence (C++ allocator), fill the block
-         table and context lengths into pinned buffers, copy them and the
-         slot mapping to the device (asynchronous);
-  device reshape_and_cache of the new tokens' K/V, then paged decode
-         attention (one split-KV kernel; split sequences are merged by the
-         last wave that finishes them).
+         table and context lengths into a pinned buffer;
+  device the slot mapping, block table and lengths reach the device (one
+         copy kernel; --stage gives the alternatives), then
+         reshape_and_cache of the new tokens' K/V and paged decode attention
+         (the split-KV kernel, then the kernel that merges the partial
+         states of sequences split over several waves).
 Consecutive steps cycle through R copies of the KV pool, as consecutive
 layers of a model would, so every step reads its keys and values from HBM
 and not from the 256 MB last-level cache. Inputs are resident in HBM before
@@ -51,6 +52,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--stage", choices=["kernel", "dma", "mapped"], default="kernel",
+                    help="per-step indices to the device: copied by a kernel (pkv_stage_copy), "
+                         "copied by the DMA engine (hipMemcpyAsync), or read in place from "
+                         "pinned host memory")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -90,6 +95,7 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventQuery.argtypes = [ctypes.c_void_p]
 
     def create(self, timing=True):
         e = self.ct.c_void_p()
@@ -200,18 +206,26 @@ def main():
     v_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
     out = torch.empty_like(q)
     ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
-    # Per-step host->device staging: slots (int64 [S]), then context lengths
-    # (int32 [S]) and the block table (int32 [S, maxb]) in one pinned buffer,
-    # double buffered, copied with one transfer per step.
+    # Per-step indices: slots (int64 [S]), then context lengths (int32 [S])
+    # and the block table (int32 [S, maxb]) in one pinned buffer, double
+    # buffered. "kernel": one copy kernel per step on the compute stream
+    # (starts within a few microseconds); "dma": the same copy through
+    # hipMemcpyAsync (the DMA engine, ~20 us to start on this path);
+    # "mapped": the kernels read the indices in place (pinned memory is
+    # mapped into the device's address space; slower id reads inside the
+    # attention kernel). The host refills buffer b only after the last work
+    # that read it (step t-2) is done.
     n32 = S + S * maxb
     words = S + (n32 + 1) // 2
     pinned = [torch.empty(words, dtype=torch.int64).pin_memory() for _ in range(2)]
     hip = HipEvents()
-    copied = [hip.create(timing=False), hip.create(timing=False)]
-    d_stage = torch.empty(words, dtype=torch.int64, device=dev)
-    d_slots = d_stage[:S]
-    d_lens = d_stage[S:].view(torch.int32)[:S]
-    d_table = d_stage[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
+    released = [hip.create(timing=False), hip.create(timing=False)]
+    mapped = args.stage == "mapped"
+    stage_mode = args.stage
+    stage = pinned if mapped else [torch.empty(words, dtype=torch.int64, device=dev)] * 2
+    d_slots = [x[:S] for x in stage]
+    d_lens = [x[S:].view(torch.int32)[:S] for x in stage]
+    d_table = [x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb) for x in stage]
     pairs_buf = np.empty(2 * S, dtype=np.int64)
     kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     stream = torch.cuda.current_stream()
@@ -224,24 +238,30 @@ def main():
     def step(t):
         b = t % 2
         if t >= 2:
-            hip.sync(copied[b])          # the copy that last read this staging buffer is done
+            hip.sync(released[b])        # the last reader of this pinned buffer is done
         base = pinned[b].data_ptr()
         npairs = alloc.batch_append_into(sids, ones, base, pairs_buf)
         assert npairs == 0
         alloc.fill_block_table_into(sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
         ctx_tokens.append(int(pinned[b][S:].view(torch.int32)[:S].sum()))
-        d_stage.copy_(pinned[b], non_blocking=True)
-        hip.record(copied[b], sh)
+        if stage_mode == "kernel":
+            pkv.stage_copy(stage[b], pinned[b])
+            hip.record(released[b], sh)
+        elif stage_mode == "dma":
+            stage[b].copy_(pinned[b], non_blocking=True)
+            hip.record(released[b], sh)
         kc, vc = pools[t % len(pools)]
         e0, e1, e2, e3 = ev[t]
         hip.record(e0, sh)
-        pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots)
+        pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots[b])
         hip.record(e1, sh)
         # decode = split-KV kernel, then merge kernel (timed apart)
-        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="split")
+        pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, phase="split")
         hip.record(e2, sh)
-        pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws, phase="merge")
+        pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, phase="merge")
         hip.record(e3, sh)
+        if mapped:
+            hip.record(released[b], sh)
 
     for t in range(args.warmup):
         step(t)
@@ -293,7 +313,7 @@ def main():
                    if w.name == "llama" else w.name,
                    "num_seqs": S, "mean_context_tokens": round(float(kv_bytes.mean() / kv_bytes_per_token / S), 1),
                    "kv_bytes_per_step": int(kv_bytes.mean()), "pool_copies_cycled": len(pools),
-                   "parallelism": "single GPU"},
+                   "index_staging": args.stage, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),

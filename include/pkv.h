@@ -152,7 +152,12 @@ int pkv_blocks_for_bytes(int64_t bytes, int32_t num_kv_heads, int32_t head_dim, 
                          int32_t* out);
 
 /* ------------------------------------------------------------------------ */
-/* Device kernels (asynchronous on `stream`). */
+/* Device kernels (asynchronous on `stream`).
+ * Index arrays (slot_mapping, pairs, block_table, context_lens, cu_q_lens)
+ * may live in device memory or in pinned, mapped host memory (hipHostMalloc):
+ * the kernels read them in place, so the host must leave them unchanged
+ * until the call's kernels have finished on the stream. Every other pointer
+ * is device memory. */
 
 /* Scatter new tokens into the pools through the slot mapping ["vLLM: what
  * PagedAttention turned into", "The problem PagedAttention was actually
@@ -178,6 +183,16 @@ int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
                     int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                     void* stream);
+
+/* Copy the per-step index arrays (slot mapping, context lengths, block table)
+ * to the device with a kernel on `stream`: the table is rebuilt by the host
+ * every step and mirrored to the device ["vLLM: what PagedAttention turned
+ * into", section "The problem PagedAttention was actually solving"], and for
+ * copies of this size a kernel starts sooner than the DMA engine. dst: device
+ * memory; src: pinned host memory or device memory; both 16-byte aligned, not
+ * overlapping; `bytes` may be any size. The host must leave src unchanged
+ * until the copy has run. */
+int pkv_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /* Workspace bytes pkv_paged_attention_decode needs for these sizes on the
  * current device (split-KV partial results and bookkeeping). The size does

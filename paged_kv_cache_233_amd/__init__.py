@@ -67,6 +67,7 @@ _SIGNATURES = {
     "pkv_blocks_for_bytes": ([_c_i64, _c_i32, _c_i32, _c_i32, _c_p], ctypes.c_int),
     "pkv_reshape_and_cache": ([_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_p], ctypes.c_int),
+    "pkv_stage_copy": ([_c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p],
                         ctypes.c_int),
     "pkv_decode_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)],
@@ -262,6 +263,19 @@ def _dev(t, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _idx(t, name: str, dtype):
+    """An index argument (slot mapping, block table, lengths, cu_q_lens):
+    a device tensor, or a pinned host tensor that the kernels read in place
+    (pinned host memory is mapped into the device's address space)."""
+    if not t.is_cuda and not t.is_pinned():
+        raise Error(ERR_INVALID_ARG, "%s must be a device tensor or pinned host memory" % name)
+    if not t.is_contiguous():
+        raise Error(ERR_INVALID_ARG, "%s must be contiguous" % name)
+    if t.dtype != dtype:
+        raise Error(ERR_INVALID_ARG, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
 def _stream(stream) -> int:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -290,8 +304,21 @@ def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None)
         raise Error(ERR_INVALID_ARG, "slot_mapping must hold %d entries" % t)
     _check(library().pkv_reshape_and_cache(
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
-        _dev(v_new, "v_new"), hkv * d, _dev(slot_mapping, "slot_mapping", torch.int64), t, nb, hkv, d,
+        _dev(v_new, "v_new"), hkv * d, _idx(slot_mapping, "slot_mapping", torch.int64), t, nb, hkv, d,
         _dtype_code(k_cache), _stream(stream)))
+
+
+def stage_copy(dst, src, stream=None) -> None:
+    """Copy src (pinned host or device tensor) into the device tensor dst
+    (same number of bytes) with a kernel on the stream."""
+    if not dst.is_cuda or not dst.is_contiguous():
+        raise Error(ERR_INVALID_ARG, "dst must be a contiguous device tensor")
+    if not (src.is_cuda or src.is_pinned()) or not src.is_contiguous():
+        raise Error(ERR_INVALID_ARG, "src must be a contiguous device or pinned host tensor")
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != nbytes:
+        raise Error(ERR_INVALID_ARG, "dst and src sizes differ")
+    _check(library().pkv_stage_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
@@ -340,7 +367,7 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
           "merge": library().pkv_paged_attention_decode_merge}[phase]
     _check(fn(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_table, "block_table", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32),
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -371,8 +398,8 @@ def prefill_chunk(out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
     _check(library().pkv_paged_attention_prefill_chunk(
-        _dev(out, "out"), _dev(q, "q"), _dev(cu_q_lens, "cu_q_lens", torch.int32),
-        _dev(context_lens, "context_lens", torch.int32), _dev(block_table, "block_table", torch.int32),
+        _dev(out, "out"), _dev(q, "q"), _idx(cu_q_lens, "cu_q_lens", torch.int32),
+        _idx(context_lens, "context_lens", torch.int32), _idx(block_table, "block_table", torch.int32),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), c, int(q.shape[0]), nb,
         int(block_table.shape[1]), int(max_q_len), int(q.shape[1]), hkv, d, float(scale),
         _dtype_code(q), ws_ptr, ws_bytes, _stream(stream)))

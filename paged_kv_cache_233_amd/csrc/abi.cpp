@@ -110,6 +110,18 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t 
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "copy_blocks launch");
 }
 
+int pkv_stage_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  pkv::clear_error();
+  if (bytes == 0) return PKV_OK;
+  if (!dst || !src) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (((uintptr_t)dst | (uintptr_t)src) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "dst and src must be 16-byte aligned");
+  if ((uintptr_t)dst < (uintptr_t)src + bytes && (uintptr_t)src < (uintptr_t)dst + bytes)
+    return fail(PKV_ERR_INVALID_ARG, "dst and src overlap");
+  hipError_t err = pkv::launch_stage_copy(dst, src, bytes, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "stage_copy launch");
+}
+
 int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, size_t* out) {
   pkv::clear_error();

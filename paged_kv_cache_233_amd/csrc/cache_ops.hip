@@ -8,6 +8,8 @@
 // row for one head is head_dim*elem bytes (128, 256 or 512), so every thread
 // reads and writes aligned 16-byte pieces and a wave covers 1 KiB of
 // consecutive bytes on both sides.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace {
@@ -60,9 +62,32 @@ copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
   }
 }
 
+// Plain copy of the per-step index arrays (slot mapping, lengths, block
+// table) from pinned host memory into device memory: 16-byte pieces on a
+// grid-stride loop, then the bytes of a ragged tail.
+__global__ void __launch_bounds__(256)
+stage_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, int64_t vecs,
+                  char* __restrict__ dst_tail, const char* __restrict__ src_tail, int32_t tail) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vecs; i += stride)
+    dst[i] = src[i];
+  if (blockIdx.x == 0 && (int32_t)threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+}
+
 }  // namespace
 
 namespace pkv {
+
+hipError_t launch_stage_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t vecs = (int64_t)(bytes / 16);
+  const int32_t tail = (int32_t)(bytes % 16);
+  const int64_t grid = std::min<int64_t>(std::max<int64_t>((vecs + 255) / 256, 1), 1024);
+  hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (uint4*)dst,
+                     (const uint4*)src, vecs, (char*)dst + vecs * 16,
+                     (const char*)src + vecs * 16, tail);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,
                                     const void* v_new, int64_t token_stride,

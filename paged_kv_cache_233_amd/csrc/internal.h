@@ -29,6 +29,7 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
                                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                                     hipStream_t stream);
 
+hipError_t launch_stage_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                               int32_t dtype, hipStream_t stream);

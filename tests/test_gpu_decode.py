@@ -284,3 +284,72 @@ def test_decode_phases_equal_whole_call():
     pkv.decode(*args, phase="merge")
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), nat["decode"].view(torch.int16))
+
+
+def test_index_arrays_in_pinned_host_memory():
+    """Slot mapping, block table and lengths read in place from pinned host
+    memory give exactly the results of device copies, also when the same
+    pinned buffer is refilled between calls."""
+    _announce("pinned index arrays")
+    w = workloads.custom("pin", 34, [1500, 33, 700, 2048, 9, 400], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    nat = run_native(w, prefill=False)
+    dec = w.decode_seqs
+    q = torch.cat([w.seq_q(s) for s in dec]).cuda()
+    ws = pkv.decode_workspace(len(dec), 32, 8, 128)
+    table_p = torch.from_numpy(nat["decode_table"].copy()).pin_memory()
+    lens_p = torch.from_numpy(nat["decode_lens"].copy()).pin_memory()
+    out = torch.empty_like(q)
+    pkv.decode(out, q, nat["k_cache"], nat["v_cache"], table_p, lens_p, w.scale, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), nat["decode"].view(torch.int16))
+    # refill the same pinned memory with the sequences in reverse order (a
+    # different batch: its split-KV partition, and so its rounding, differ;
+    # compare with the same batch through device copies)
+    rt = nat["decode_table"][::-1].copy()
+    rl = nat["decode_lens"][::-1].copy()
+    table_p.copy_(torch.from_numpy(rt))
+    lens_p.copy_(torch.from_numpy(rl))
+    rq = torch.flip(q, [0]).contiguous()
+    pkv.decode(out, rq, nat["k_cache"], nat["v_cache"], table_p, lens_p, w.scale, ws)
+    ref = torch.empty_like(q)
+    pkv.decode(ref, rq, nat["k_cache"], nat["v_cache"], torch.from_numpy(rt).cuda(),
+               torch.from_numpy(rl).cuda(), w.scale, pkv.decode_workspace(len(dec), 32, 8, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert not torch.equal(out.view(torch.int16), nat["decode"].view(torch.int16))
+    # reshape_and_cache with a pinned slot mapping
+    rng = np.random.default_rng(5)
+    nb = nat["k_cache"].shape[0]
+    slots = rng.permutation(nb * 16)[:96].astype(np.int64)
+    k_new = torch.randn((96, 8, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    v_new = torch.randn((96, 8, 128), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).cuda()
+    kc1, vc1 = nat["k_cache"].clone(), nat["v_cache"].clone()
+    kc2, vc2 = nat["k_cache"].clone(), nat["v_cache"].clone()
+    pkv.reshape_and_cache(kc1, vc1, k_new, v_new, torch.from_numpy(slots).cuda())
+    pkv.reshape_and_cache(kc2, vc2, k_new, v_new, torch.from_numpy(slots).pin_memory())
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    # an unpinned host tensor is refused
+    with pytest.raises(pkv.Error):
+        pkv.decode(out, q, nat["k_cache"], nat["v_cache"], torch.from_numpy(nat["decode_table"]),
+                   lens_p, w.scale, ws)
+
+
+def test_stage_copy_bit_exact():
+    """pkv_stage_copy from pinned host and from device memory, whole 16-byte
+    pieces and ragged tails, leaves the bytes after the range untouched."""
+    _announce("stage_copy")
+    rng = np.random.default_rng(8)
+    for nbytes in (16, 70_144, 70_150, 1_000_003):
+        src = torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).pin_memory()
+        dst = torch.full((nbytes + 32,), 0xAB, dtype=torch.uint8, device="cuda")
+        pkv.stage_copy(dst[:nbytes], src)
+        dsrc = src.cuda()
+        dst2 = torch.full((nbytes + 32,), 0xCD, dtype=torch.uint8, device="cuda")
+        pkv.stage_copy(dst2[:nbytes], dsrc)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes].cpu(), src)
+        assert torch.equal(dst2[:nbytes], dsrc)
+        assert (dst[nbytes:] == 0xAB).all() and (dst2[nbytes:] == 0xCD).all()

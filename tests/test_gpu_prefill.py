@@ -133,3 +133,21 @@ def test_prefill_full_mixed_workload():
     stats = assert_close(nat["prefill"], ora["prefill"], "bf16", "mixed prefill")
     assert_close(nat["decode"][[0, 9]], ora["decode"], "bf16", "mixed decode")
     print("mixed prefill error", stats)
+
+
+def test_prefill_index_arrays_in_pinned_host_memory():
+    """cu_q_lens, context lengths and block table read in place from pinned
+    host memory give exactly the device-copy result."""
+    w = workloads.custom("pfp", 55, [60], chunks=[(40, 70), (0, 33)], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, dtype="bf16")
+    _announce("prefill pinned index arrays")
+    nat = run_native(w)
+    q = torch.cat([w.seq_q(s) for s in w.chunk_seqs]).cuda()
+    cu = nat["prefill_cu"]
+    out = torch.empty_like(q)
+    pkv.prefill_chunk(out, q, torch.from_numpy(cu).pin_memory(),
+                      torch.from_numpy(nat["prefill_lens"].copy()).pin_memory(),
+                      torch.from_numpy(nat["prefill_table"].copy()).pin_memory(),
+                      nat["k_cache"], nat["v_cache"], int(max(s.new_tokens for s in w.chunk_seqs)), w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), nat["prefill"].view(torch.int16))

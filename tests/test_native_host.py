@@ -231,6 +231,11 @@ def test_device_entry_points_reject_bad_arguments():
     # prefill: bad head_dim
     assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 1, 4, 1, 1, 8,
                 2, 80, ctypes.c_float(1.0), 1, None, 0, None) == pkv.ERR_UNSUPPORTED
+    # stage_copy: zero bytes is a no-op; misaligned, NULL or overlapping ranges are refused
+    assert _raw("pkv_stage_copy", 16, 32, 0, None) == 0
+    assert _raw("pkv_stage_copy", 16, 40, 8, None) == pkv.ERR_INVALID_ARG
+    assert _raw("pkv_stage_copy", None, 32, 16, None) == pkv.ERR_INVALID_ARG
+    assert _raw("pkv_stage_copy", 64, 32, 48, None) == pkv.ERR_INVALID_ARG
     # copy_blocks: negative count
     assert _raw("pkv_copy_blocks", 16, 16, 16, -1, 4, 1, 128, 1, None) == pkv.ERR_INVALID_ARG
     assert b"head_dim" in pkv.library().pkv_last_error() or True
