@@ -1,0 +1,78 @@
+"""A whole decode step (index staging, reshape_and_cache, split-KV and merge
+kernels) captured as one HIP graph and replayed: every replay equals the
+same step run eagerly, bit for bit. The entry points never synchronise with
+the host or allocate, which is what capture needs ("(2) vLLM Internals: From
+PagedAttention to Removing PagedAttention", section 4.2, on capturing a whole
+decode step as one graph)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_233_amd as pkv
+import workloads
+from tests.pipeline import run_native
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_graph_replays_equal_eager():
+    print("[gpu] graph capture of a decode step", flush=True)
+    w = workloads.custom("gr", 60, [700, 1500, 33, 2048], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    nat = run_native(w, prefill=False)
+    dec = w.decode_seqs
+    S = len(dec)
+    table, lens = nat["decode_table"], nat["decode_lens"]
+    maxb = table.shape[1]
+    nb = nat["k_cache"].shape[0]
+    # pinned staging: slots int64 [S] | lens int32 [S] | table int32 [S, maxb]
+    words = S + (S + S * maxb + 1) // 2
+    pinned = torch.zeros(words, dtype=torch.int64).pin_memory()
+    stage = torch.empty(words, dtype=torch.int64, device="cuda")
+    q = torch.empty((S, 32, 128), dtype=torch.bfloat16, device="cuda")
+    k_new = torch.empty((S, 8, 128), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.empty_like(k_new)
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(S, 32, 8, 128)
+    kc, vc = nat["k_cache"].clone(), nat["v_cache"].clone()
+
+    def fill(slots, ln, tb):
+        pinned[:S] = torch.from_numpy(slots)
+        p32 = pinned[S:].view(torch.int32)
+        p32[:S] = torch.from_numpy(ln)
+        p32[S:S + S * maxb] = torch.from_numpy(tb.reshape(-1))
+
+    def step(kc_, vc_, out_):
+        pkv.stage_copy(stage, pinned)
+        st32 = stage[S:].view(torch.int32)
+        pkv.reshape_and_cache(kc_, vc_, k_new, v_new, stage[:S])
+        args = (out_, q, kc_, vc_, st32[S:S + S * maxb].view(S, maxb), st32[:S], w.scale, ws)
+        pkv.decode(*args, phase="split")
+        pkv.decode(*args, phase="merge")
+
+    rng = np.random.default_rng(0)
+    g = torch.cuda.CUDAGraph()
+    fill(np.full(S, -1, dtype=np.int64), lens, table)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step(kc, vc, out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        # new inputs for this replay: query, new tokens written to random free
+        # slots of the pool, lengths cut or kept
+        q.copy_(torch.randn(q.shape, generator=torch.Generator().manual_seed(rep)).to(torch.bfloat16))
+        k_new.copy_(torch.randn(k_new.shape, generator=torch.Generator().manual_seed(10 + rep)).to(torch.bfloat16))
+        v_new.copy_(torch.randn(v_new.shape, generator=torch.Generator().manual_seed(20 + rep)).to(torch.bfloat16))
+        slots = rng.choice(np.arange(16, nb * 16), S, replace=False).astype(np.int64)
+        ln = np.minimum(lens, rng.integers(1, lens + 1)).astype(np.int32)
+        fill(slots, ln, table)
+        kc_ref, vc_ref = kc.clone(), vc.clone()
+        ref = torch.empty_like(out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(kc_ref, vc_ref, ref)          # the same step, eagerly
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        assert torch.equal(kc.view(torch.int16), kc_ref.view(torch.int16)), rep
+        assert torch.equal(vc.view(torch.int16), vc_ref.view(torch.int16)), rep
