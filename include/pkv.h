@@ -128,6 +128,51 @@ int pkv_batch_append(pkv_allocator* a, const int64_t* seq_ids, const int32_t* n_
 int pkv_seq_fork(pkv_allocator* a, int64_t parent_id, int64_t child_id);
 /* Release a sequence (tail first, see above). */
 int pkv_seq_free(pkv_allocator* a, int64_t seq_id);
+/* ---- Prefix caching (content-addressed blocks) ----
+ * ["vLLM: what PagedAttention turned into", sections "The block pool, and the
+ * two tricks in it" and "What a block hash actually is"]. A full block whose
+ * token ids have been recorded gets a chained content hash (see
+ * pkv_hash_block_tokens) and enters a hash -> block map, keyed by the hash
+ * followed by the KV-cache group id (4 bytes big endian; one group, 0). If
+ * another block already holds that key, the new block stays unhashed. A
+ * freed block with a hash keeps it and goes to the back of the free queue
+ * (FIFO: least recently freed is evicted first); it leaves the map only when
+ * the queue hands it out again (lazy eviction). Freed blocks without a hash
+ * go to the front (LIFO). Off by default. */
+/* Switch prefix caching on (enabled != 0) or off; only while no sequence
+ * exists. Either way the map is emptied. */
+int pkv_allocator_enable_prefix_caching(pkv_allocator* a, int32_t enabled);
+/* Create a sequence for a prompt of n_tokens token ids and attach the
+ * longest run of cached full blocks from its start (at most
+ * max_cached_tokens tokens; < 0 means no limit), walking block by block and
+ * stopping at the first miss (sound because the hashes chain). A cached block
+ * that is free is taken back out of the free queue. *out_cached_tokens
+ * (may be NULL) receives the number of tokens attached (a multiple of 16);
+ * the sequence's length is that number and its first that many token ids are
+ * recorded. extra_key is folded into the first block's hash only (a per-tenant
+ * salt: different keys never share blocks). With caching off, the sequence
+ * starts empty. */
+int pkv_seq_add_cached(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                       uint64_t extra_key, int32_t max_cached_tokens, int32_t* out_cached_tokens);
+/* Record the ids of the sequence's next n tokens (in order, within its
+ * appended length; call once their K/V are written). Every block this
+ * fills gets its chained hash and, with caching on, enters the map. */
+int pkv_seq_record_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n);
+/* The content hash of a block: out[32] and *has_hash (0: none, out zeroed). */
+int pkv_block_hash(pkv_allocator* a, int32_t block, uint8_t* out, int32_t* has_hash);
+/* Blocks in the hash map, prefix lookups made, and blocks they attached
+ * (any pointer may be NULL). */
+int pkv_prefix_cache_stats(pkv_allocator* a, int32_t* cached_blocks, int64_t* lookups,
+                           int64_t* hit_blocks);
+/* Chained block hash: SHA-256 of parent_hash (32 bytes; NULL for a first
+ * block, which uses the fixed seed hash SHA-256("pkv none hash")), the 16
+ * token ids as little-endian int32 and extra_key as little-endian uint64;
+ * out[32]. */
+int pkv_hash_block_tokens(const uint8_t* parent_hash, const int32_t* tokens, uint64_t extra_key,
+                          uint8_t* out);
+/* SHA-256 (FIPS 180-4) of n bytes into out[32]. */
+int pkv_sha256(const void* data, size_t n, uint8_t* out);
+
 /* Length of a sequence in tokens. */
 int pkv_seq_len(pkv_allocator* a, int64_t seq_id, int64_t* out);
 /* Dense block table for n sequences: table[n][max_blocks] (int32, row-major)

@@ -11,8 +11,16 @@ Policy, from the pages (cited by page title and section):
   PagedAttention turned into", "The block pool, and the two tricks in it").
   Block tables are padded with it.
 * Blocks freed with no content hash go to the front of the free queue and
-  are reused first (LIFO) (same section). This model keeps no hashes, so
-  every freed block takes that path.
+  are reused first (LIFO); blocks freed with a hash go to the back (FIFO),
+  keep their hash and stay reusable until the queue hands them out again,
+  which is when they are evicted (lazily) (same section).
+* Prefix caching (optional): a full block's hash chains its parent's hash,
+  its token ids and extra keys, so it names a prefix ending at the block;
+  lookups walk a prompt's full blocks from the start and stop at the first
+  miss; the extra key (a tenant salt) enters the first block only ("vLLM:
+  what PagedAttention turned into", "What a block hash actually is"). The
+  map key is the hash followed by the KV-cache group id, 4 bytes big endian
+  ("The block pool, and the two tricks in it").
 * A request's blocks are handed back tail first, so its last block is the
   first to be reused and its first block the last (same section).
 * Identical prefixes share physical blocks by reference counting, and a
@@ -28,18 +36,35 @@ Policy, from the pages (cited by page title and section):
 
 Readings where the pages are silent: the initial free queue is 0, 1, ...,
 NB-1 unless an explicit order is installed; a batch of freed blocks is placed
-at the front in the order it was visited (tail first), so the tail is
-reused first; the copy-on-write trigger is an append into a partially filled
-last block whose refcount exceeds one; a full shared block is never copied.
+at the front (or, hashed, at the back) in the order it was visited (tail
+first), so the tail is reused (or evicted) first; the copy-on-write trigger
+is an append into a partially filled last block whose refcount exceeds one; a
+full shared block is never copied. The hash is SHA-256 over the parent hash
+(32 bytes; for a first block the hash of the fixed string "pkv none hash"),
+the 16 token ids as little-endian int32 and the extra key as little-endian
+uint64; a block whose key another block already holds stays unhashed; token
+ids are recorded per sequence in order and a block is hashed when its
+sixteenth id is recorded.
 """
 from __future__ import annotations
 
 import collections
-from typing import Dict, List, Sequence, Tuple
+import hashlib
+import struct
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 BLOCK = 16
+NONE_HASH = hashlib.sha256(b"pkv none hash").digest()
+GROUP_ID = (0).to_bytes(4, "big")
+
+
+def block_hash(parent: Optional[bytes], tokens: Sequence[int], extra: int = 0) -> bytes:
+    """Chained content hash of one full block."""
+    msg = (parent if parent is not None else NONE_HASH)
+    msg += np.asarray(tokens, dtype="<i4").tobytes() + struct.pack("<Q", int(extra))
+    return hashlib.sha256(msg).digest()
 
 
 class OutOfBlocks(Exception):
@@ -56,6 +81,14 @@ class AllocatorModel:
         self.ref = [0] * num_blocks
         self.blocks: Dict[int, List[int]] = {}
         self.length: Dict[int, int] = {}
+        # prefix cache
+        self.caching = False
+        self.hash: Dict[int, bytes] = {}          # block -> its hash (cached blocks)
+        self.parent_of: Dict[int, Optional[bytes]] = {}
+        self.cache: Dict[bytes, int] = {}         # hash + group id -> block
+        self.chain: Dict[int, dict] = {}          # sequence -> recorded ids state
+        self.lookups = 0
+        self.hit_blocks = 0
 
     # ----------------------------------------------------------------- setup
     def set_free_order(self, order: Sequence[int]) -> None:
@@ -64,7 +97,29 @@ class AllocatorModel:
         order = [int(x) for x in order]
         if self.blocks or sorted(order) != list(range(1, self.num_blocks)):
             raise ValueError("free order must permute 1..NB-1 while the pool is empty")
+        self._clear_cache()
         self.free = collections.deque(order)
+
+    def _clear_cache(self) -> None:
+        self.hash.clear()
+        self.parent_of.clear()
+        self.cache.clear()
+
+    def enable_caching(self, enabled: bool = True) -> None:
+        if self.blocks:
+            raise ValueError("only while no sequence exists")
+        self._clear_cache()
+        self.caching = bool(enabled)
+
+    def _pop(self) -> int:
+        """Take the front block; a cached one is evicted now (lazily)."""
+        b = self.free.popleft()
+        if b in self.hash:
+            key = self.hash.pop(b) + GROUP_ID
+            self.parent_of.pop(b)
+            if self.cache.get(key) == b:
+                del self.cache[key]
+        return b
 
     # ------------------------------------------------------------- sequences
     def add(self, sid: int) -> None:
@@ -72,6 +127,58 @@ class AllocatorModel:
             raise KeyError("sequence exists")
         self.blocks[sid] = []
         self.length[sid] = 0
+        self.chain[sid] = {"recorded": 0, "parent": None, "pending": [], "salt": 0}
+
+    def add_cached(self, sid: int, tokens: Sequence[int], salt: int = 0, max_cached: int = -1) -> int:
+        """New sequence for a prompt: attach the longest run of cached full
+        blocks from its start; returns the tokens attached."""
+        if sid in self.blocks:
+            raise KeyError("sequence exists")
+        tokens = [int(t) for t in tokens]
+        limit = len(tokens) if max_cached < 0 else min(len(tokens), max_cached)
+        full = limit // BLOCK if self.caching else 0
+        parent = None
+        got: List[int] = []
+        for k in range(full):
+            h = block_hash(parent, tokens[k * BLOCK:(k + 1) * BLOCK], salt if k == 0 else 0)
+            b = self.cache.get(h + GROUP_ID)
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            got.append(b)
+            parent = h
+        self.blocks[sid] = got
+        self.length[sid] = BLOCK * len(got)
+        self.chain[sid] = {"recorded": BLOCK * len(got), "parent": parent, "pending": [],
+                           "salt": int(salt)}
+        self.lookups += 1
+        self.hit_blocks += len(got)
+        return BLOCK * len(got)
+
+    def record_tokens(self, sid: int, tokens: Sequence[int]) -> None:
+        """Ids of the sequence's next tokens; a block whose sixteenth id
+        arrives is hashed and, with caching on, enters the map."""
+        st = self.chain[sid]
+        if st["recorded"] + len(tokens) > self.length[sid]:
+            raise ValueError("recording beyond the sequence's length")
+        for t in tokens:
+            st["pending"].append(int(t))
+            st["recorded"] += 1
+            if st["recorded"] % BLOCK == 0:
+                k = st["recorded"] // BLOCK - 1
+                h = block_hash(st["parent"], st["pending"], st["salt"] if k == 0 else 0)
+                self._register(self.blocks[sid][k], h, st["parent"])
+                st["parent"] = h
+                st["pending"] = []
+
+    def _register(self, b: int, h: bytes, parent: Optional[bytes]) -> None:
+        if not self.caching or b in self.hash or (h + GROUP_ID) in self.cache:
+            return
+        self.hash[b] = h
+        self.parent_of[b] = parent
+        self.cache[h + GROUP_ID] = b
 
     def _needs(self, sid: int, n: int) -> Tuple[bool, int]:
         """(copy-on-write needed, new blocks needed) to append n tokens."""
@@ -86,13 +193,13 @@ class AllocatorModel:
         pairs = []
         if cow:
             old = blocks[-1]
-            new = self.free.popleft()
+            new = self._pop()
             self.ref[new] = 1
             self.ref[old] -= 1
             blocks[-1] = new
             pairs.append((old, new))
         for _ in range(grow):
-            b = self.free.popleft()
+            b = self._pop()
             self.ref[b] = 1
             blocks.append(b)
         start = self.length[sid]
@@ -135,22 +242,34 @@ class AllocatorModel:
             raise KeyError("sequence exists")
         self.blocks[child] = list(self.blocks[parent])
         self.length[child] = self.length[parent]
+        st = self.chain[parent]
+        self.chain[child] = {"recorded": st["recorded"], "parent": st["parent"],
+                             "pending": list(st["pending"]), "salt": st["salt"]}
         for b in self.blocks[child]:
             self.ref[b] += 1
 
     def free_seq(self, sid: int) -> None:
         """Release a sequence: its blocks are visited tail first; those whose
-        refcount drops to zero go to the front of the free queue in that
-        order."""
+        refcount drops to zero go to the front of the free queue (no hash)
+        or to its back (hashed), each pile in visiting order."""
         if sid not in self.blocks:
             raise KeyError("no such sequence")
-        released = []
+        front, back = [], []
         for b in reversed(self.blocks.pop(sid)):
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                released.append(b)
+                (back if b in self.hash else front).append(b)
         del self.length[sid]
-        self.free.extendleft(reversed(released))
+        del self.chain[sid]
+        self.free.extendleft(reversed(front))
+        self.free.extend(back)
+
+    def block_hash_of(self, b: int) -> Optional[bytes]:
+        return self.hash.get(b)
+
+    def cache_stats(self) -> dict:
+        return {"cached_blocks": len(self.cache), "lookups": self.lookups,
+                "hit_blocks": self.hit_blocks}
 
     # ----------------------------------------------------------------- views
     def block_table(self, sids: Sequence[int], max_blocks: int):

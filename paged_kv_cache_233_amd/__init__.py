@@ -60,6 +60,13 @@ _SIGNATURES = {
     "pkv_seq_fork": ([_c_p, _c_i64, _c_i64], ctypes.c_int),
     "pkv_seq_free": ([_c_p, _c_i64], ctypes.c_int),
     "pkv_seq_len": ([_c_p, _c_i64, _c_p], ctypes.c_int),
+    "pkv_allocator_enable_prefix_caching": ([_c_p, _c_i32], ctypes.c_int),
+    "pkv_seq_add_cached": ([_c_p, _c_i64, _c_p, _c_i32, ctypes.c_uint64, _c_i32, _c_p], ctypes.c_int),
+    "pkv_seq_record_tokens": ([_c_p, _c_i64, _c_p, _c_i32], ctypes.c_int),
+    "pkv_block_hash": ([_c_p, _c_i32, _c_p, _c_p], ctypes.c_int),
+    "pkv_prefix_cache_stats": ([_c_p, _c_p, _c_p, _c_p], ctypes.c_int),
+    "pkv_hash_block_tokens": ([_c_p, _c_p, ctypes.c_uint64, _c_p], ctypes.c_int),
+    "pkv_sha256": ([_c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
     "pkv_fill_block_table": ([_c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p], ctypes.c_int),
     "pkv_block_refcount": ([_c_p, _c_i32, _c_p], ctypes.c_int),
     "pkv_num_free_blocks": ([_c_p, _c_p], ctypes.c_int),
@@ -134,9 +141,29 @@ def _ptr(a: np.ndarray) -> int:
 
 
 # --------------------------------------------------------------- allocator
+def sha256(data: bytes) -> bytes:
+    """SHA-256 of a byte string (the library's own implementation)."""
+    buf = ctypes.create_string_buffer(bytes(data), max(1, len(data)))
+    out = ctypes.create_string_buffer(32)
+    _check(library().pkv_sha256(buf, len(data), out))
+    return out.raw
+
+
+def hash_block_tokens(parent: Optional[bytes], tokens, extra_key: int = 0) -> bytes:
+    """Chained content hash of one full block of 16 token ids."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    if t.size != BLOCK_SIZE:
+        raise Error(ERR_INVALID_ARG, "a block holds %d token ids" % BLOCK_SIZE)
+    par = None if parent is None else ctypes.create_string_buffer(bytes(parent), 32)
+    out = ctypes.create_string_buffer(32)
+    _check(library().pkv_hash_block_tokens(par, _ptr(t), int(extra_key), out))
+    return out.raw
+
+
 class Allocator:
     """Host block allocator (C++): null block 0, LIFO reuse, tail-first
-    release, refcounted sharing with copy-on-write."""
+    release, refcounted sharing with copy-on-write, optional prefix caching
+    (content-hashed blocks, FIFO for cached free blocks, lazy eviction)."""
 
     def __init__(self, num_blocks: int):
         self._lib = library()
@@ -162,6 +189,37 @@ class Allocator:
 
     def add(self, sid: int) -> None:
         _check(self._lib.pkv_seq_add(self._h, int(sid)))
+
+    # ------------------------------------------------------- prefix caching
+    def enable_prefix_caching(self, enabled: bool = True) -> None:
+        _check(self._lib.pkv_allocator_enable_prefix_caching(self._h, 1 if enabled else 0))
+
+    def add_cached(self, sid: int, tokens, extra_key: int = 0, max_cached: int = -1) -> int:
+        """New sequence for a prompt; attaches its longest cached prefix of
+        full blocks and returns the number of tokens attached."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        got = _c_i32(0)
+        _check(self._lib.pkv_seq_add_cached(self._h, int(sid), _ptr(t) if t.size else None,
+                                            int(t.size), int(extra_key), int(max_cached),
+                                            ctypes.byref(got)))
+        return int(got.value)
+
+    def record_tokens(self, sid: int, tokens) -> None:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(self._lib.pkv_seq_record_tokens(self._h, int(sid), _ptr(t) if t.size else None,
+                                               int(t.size)))
+
+    def block_hash(self, block: int) -> Optional[bytes]:
+        out = ctypes.create_string_buffer(32)
+        has = _c_i32(0)
+        _check(self._lib.pkv_block_hash(self._h, int(block), out, ctypes.byref(has)))
+        return out.raw if has.value else None
+
+    def prefix_cache_stats(self) -> dict:
+        c, l, h = _c_i32(0), _c_i64(0), _c_i64(0)
+        _check(self._lib.pkv_prefix_cache_stats(self._h, ctypes.byref(c), ctypes.byref(l),
+                                                ctypes.byref(h)))
+        return {"cached_blocks": c.value, "lookups": l.value, "hit_blocks": h.value}
 
     def append(self, sid: int, n: int, max_pairs: int = 1) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
         return self.batch_append([sid], [n], max_pairs)

@@ -3,18 +3,53 @@
 // Policy (see pkv.h for the full contract) follows "vLLM: what PagedAttention
 // turned into", section "The block pool, and the two tricks in it": the first
 // block popped from the free queue becomes the null block; freed blocks
-// without a content hash go to the front of the queue (LIFO), a request's
-// blocks handed back tail first; the free queue is an intrusive doubly linked
-// list with sentinel head and tail stored in two int32 arrays, so removal
-// anywhere is O(1) and no per-operation heap objects are created. Sharing by
-// refcount and copy-on-write follow "(2) vLLM Internals: From PagedAttention
-// to Removing PagedAttention", section 1.2 "Three Direct Wins".
+// without a content hash go to the front of the queue (LIFO), freed blocks
+// with one to the back (FIFO, so cached prefixes are evicted least recently
+// freed first), a request's blocks handed back tail first; the free queue is
+// an intrusive doubly linked list with sentinel head and tail stored in two
+// int32 arrays, so removal anywhere is O(1) and no per-operation heap objects
+// are created. Sharing by refcount and copy-on-write follow "(2) vLLM
+// Internals: From PagedAttention to Removing PagedAttention", section 1.2
+// "Three Direct Wins".
+//
+// Prefix caching (optional; same page, sections "The block pool, and the two
+// tricks in it" and "What a block hash actually is"): a full block whose
+// token ids are known gets a chained content hash and enters a hash -> block
+// map; when freed it keeps the hash and stays reusable until the free queue
+// hands it out again, at which point it is evicted (lazily); a new sequence
+// takes the longest run of cached full blocks of its prompt, stopping at the
+// first miss.
 #include <algorithm>
+#include <array>
+#include <cstring>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
 #include "internal.h"
+
+namespace {
+
+typedef std::array<uint8_t, 32> Hash;
+// Map key: the block hash followed by the KV-cache group id, 4 bytes big
+// endian (one group here: 0).
+typedef std::array<uint8_t, 36> Key;
+
+struct KeyHasher {
+  size_t operator()(const Key& k) const {
+    uint64_t v;
+    std::memcpy(&v, k.data(), sizeof(v));
+    return (size_t)v;
+  }
+};
+
+Key make_key(const Hash& h) {
+  Key k{};
+  std::copy(h.begin(), h.end(), k.begin());
+  return k;
+}
+
+}  // namespace
 
 struct pkv_allocator {
   int32_t nb = 0;
@@ -27,12 +62,46 @@ struct pkv_allocator {
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t len = 0;
+    // content-hash chain: token ids recorded so far, hash of the last full
+    // recorded block, ids of the partly recorded block, the extra key of the
+    // first block
+    int64_t recorded = 0;
+    bool has_parent = false;
+    Hash parent{};
+    int32_t pending[pkv::kBlock] = {};
+    uint64_t salt = 0;
   };
   std::unordered_map<int64_t, Seq> seqs;
+  // prefix cache
+  bool caching = false;
+  std::vector<Hash> bhash;
+  std::vector<uint8_t> hashed;
+  std::unordered_map<Key, int32_t, KeyHasher> cached;
+  int64_t lookups = 0, hit_blocks = 0;
 
   int32_t head() const { return nb; }
   int32_t tail() const { return nb + 1; }
 
+  // Lazy eviction: a cached block leaves the map when it is reused.
+  void evict(int32_t b) {
+    auto it = cached.find(make_key(bhash[b]));
+    if (it != cached.end() && it->second == b) cached.erase(it);
+    hashed[b] = 0;
+  }
+  void clear_cache() {
+    cached.clear();
+    std::fill(hashed.begin(), hashed.end(), 0);
+  }
+  // A full block of a sequence got its hash: it enters the map unless
+  // another block already holds the same content.
+  void register_block(int32_t b, const Hash& h) {
+    if (!caching || hashed[b]) return;
+    Key k = make_key(h);
+    if (cached.count(k)) return;
+    bhash[b] = h;
+    hashed[b] = 1;
+    cached.emplace(k, b);
+  }
   void link_after(int32_t at, int32_t b) {
     int32_t n = next[at];
     next[at] = b;
@@ -52,6 +121,7 @@ struct pkv_allocator {
   int32_t pop_front() {
     int32_t b = next[head()];
     unlink(b);
+    if (hashed[b]) evict(b);
     return b;
   }
   void reset_queue(const int32_t* order, int32_t n) {
@@ -123,6 +193,8 @@ int pkv_allocator_create(int32_t num_blocks, pkv_allocator** out) {
   a->prev.assign(num_blocks + 2, -1);
   a->in_free.assign(num_blocks, 0);
   a->ref.assign(num_blocks, 0);
+  a->bhash.assign(num_blocks, Hash{});
+  a->hashed.assign(num_blocks, 0);
   std::vector<int32_t> order(num_blocks);
   for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
   a->reset_queue(order.data(), num_blocks);
@@ -152,6 +224,7 @@ int pkv_allocator_set_free_order(pkv_allocator* a, const int32_t* order, int32_t
                   a->nb - 1, i, b);
     seen[b] = 1;
   }
+  a->clear_cache();
   a->reset_queue(order, n);
   return PKV_OK;
 }
@@ -232,18 +305,112 @@ int pkv_seq_free(pkv_allocator* a, int64_t seq_id) {
   if (int e = check_handle(a)) return e;
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq_id);
-  // Visit tail first; released blocks go to the queue front in visiting
-  // order, so the tail is handed out first and the first block last.
+  // Visit tail first. Released blocks without a hash go to the queue front
+  // in visiting order, so the tail is handed out first and the first block
+  // last; released blocks with a hash go to the back in visiting order, so
+  // among cached blocks the tail is also evicted first.
   int32_t at = a->head();
   const std::vector<int32_t>& bl = it->second.blocks;
   for (size_t i = bl.size(); i-- > 0;) {
     int32_t b = bl[i];
     if (--a->ref[b] == 0) {
-      a->link_after(at, b);
-      at = b;
+      if (a->hashed[b]) {
+        a->link_after(a->prev[a->tail()], b);
+      } else {
+        a->link_after(at, b);
+        at = b;
+      }
     }
   }
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_allocator_enable_prefix_caching(pkv_allocator* a, int32_t enabled) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  if (!a->seqs.empty())
+    return fail(PKV_ERR_INVALID_ARG, "prefix caching can only be switched while no sequence exists");
+  a->clear_cache();
+  a->caching = enabled != 0;
+  return PKV_OK;
+}
+
+int pkv_seq_add_cached(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                       uint64_t extra_key, int32_t max_cached_tokens, int32_t* out_cached_tokens) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token list");
+  if (a->seqs.count(seq_id)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)seq_id);
+  pkv_allocator::Seq s;
+  s.salt = extra_key;
+  int32_t limit = max_cached_tokens < 0 ? n_tokens : std::min(n_tokens, max_cached_tokens);
+  int32_t full = a->caching ? limit / pkv::kBlock : 0;
+  Hash h;
+  for (int32_t k = 0; k < full; ++k) {
+    pkv::block_hash(s.has_parent ? s.parent.data() : nullptr, tokens + (int64_t)k * pkv::kBlock,
+                    k == 0 ? extra_key : 0, h.data());
+    auto it = a->cached.find(make_key(h));
+    if (it == a->cached.end()) break;  // chained hashes: every later block misses too
+    int32_t b = it->second;
+    if (a->ref[b] == 0) a->unlink(b);  // free but cached: revived from the queue
+    a->ref[b] += 1;
+    s.blocks.push_back(b);
+    s.parent = h;
+    s.has_parent = true;
+  }
+  s.len = s.recorded = (int64_t)s.blocks.size() * pkv::kBlock;
+  a->lookups += 1;
+  a->hit_blocks += (int64_t)s.blocks.size();
+  if (out_cached_tokens) *out_cached_tokens = (int32_t)s.len;
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_seq_record_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq_id);
+  pkv_allocator::Seq& s = it->second;
+  if (n < 0 || (n > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token list");
+  if (s.recorded + n > s.len)
+    return fail(PKV_ERR_INVALID_ARG, "sequence %lld: %lld recorded + %d > length %lld",
+                (long long)seq_id, (long long)s.recorded, n, (long long)s.len);
+  Hash h;
+  for (int32_t i = 0; i < n; ++i) {
+    s.pending[s.recorded % pkv::kBlock] = tokens[i];
+    s.recorded += 1;
+    if (s.recorded % pkv::kBlock == 0) {
+      const int64_t k = s.recorded / pkv::kBlock - 1;
+      pkv::block_hash(s.has_parent ? s.parent.data() : nullptr, s.pending, k == 0 ? s.salt : 0,
+                      h.data());
+      s.parent = h;
+      s.has_parent = true;
+      a->register_block(s.blocks[k], h);
+    }
+  }
+  return PKV_OK;
+}
+
+int pkv_block_hash(pkv_allocator* a, int32_t block, uint8_t* out, int32_t* has_hash) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  if (!out || !has_hash || block < 0 || block >= a->nb)
+    return fail(PKV_ERR_INVALID_ARG, "bad block query");
+  *has_hash = a->hashed[block];
+  std::memcpy(out, a->bhash[block].data(), 32);
+  if (!*has_hash) std::memset(out, 0, 32);
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_stats(pkv_allocator* a, int32_t* cached_blocks, int64_t* lookups,
+                           int64_t* hit_blocks) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  if (cached_blocks) *cached_blocks = (int32_t)a->cached.size();
+  if (lookups) *lookups = a->lookups;
+  if (hit_blocks) *hit_blocks = a->hit_blocks;
   return PKV_OK;
 }
 

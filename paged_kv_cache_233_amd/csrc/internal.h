@@ -20,6 +20,12 @@ int hip_fail(hipError_t e, const char* what);
 
 constexpr int kBlock = PKV_BLOCK_SIZE;
 
+// SHA-256 of n bytes; the seed hash of a first block; the chained content
+// hash of one full block (parent may be NULL for the first block).
+void sha256(const void* data, size_t n, uint8_t out[32]);
+const uint8_t* none_hash();
+void block_hash(const uint8_t* parent, const int32_t* tokens, uint64_t extra, uint8_t out[32]);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated by
 // the caller.

@@ -1,0 +1,273 @@
+"""Prefix caching in the block allocator (content-addressed blocks), on the
+CPU: the library's SHA-256 against the standard's published examples, the
+chained block hash against the oracle model (hashlib), the policy pins that
+"vLLM: what PagedAttention turned into" states (sections "The block pool,
+and the two tricks in it" and "What a block hash actually is"), and the C++
+allocator against the Python model over random operation streams."""
+import hashlib
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_233_amd as pkv
+from oracle import allocator as amodel
+
+B = amodel.BLOCK
+
+
+# ------------------------------------------------------------------ hashing
+def test_sha256_published_examples():
+    """FIPS 180-2, Appendix B: the one-block message "abc", the two-block
+    448-bit message and one million repetitions of "a"."""
+    assert pkv.sha256(b"abc").hex() == \
+        "ba7816bf8f01cfea414140de5dae2223b00361a396177a9cb410ff61f20015ad"
+    assert pkv.sha256(b"abcdbcdecdefdefgefghfghighijhijkijkljklmklmnlmnomnopnopq").hex() == \
+        "248d6a61d20638b8e5c026930c3e6039a33ce45964ff2167f6ecedd419db06c1"
+    assert pkv.sha256(b"a" * 1000000).hex() == \
+        "cdc76e5c9914fb9281a1c7e284d73e67f1809a48a497200e046d39ccc7112cd0"
+
+
+def test_sha256_padding_boundaries():
+    data = bytes(np.random.default_rng(0).integers(0, 256, 400, dtype=np.uint8))
+    for n in list(range(0, 130)) + [191, 192, 255, 256, 257, 400]:
+        assert pkv.sha256(data[:n]) == hashlib.sha256(data[:n]).digest(), n
+
+
+def test_block_hash_matches_model():
+    rng = np.random.default_rng(1)
+    parent = None
+    for i in range(40):
+        toks = rng.integers(-2**31, 2**31 - 1, B, dtype=np.int64).astype(np.int32)
+        extra = int(rng.integers(0, 2**63)) if i % 3 == 0 else 0
+        h = pkv.hash_block_tokens(parent, toks, extra)
+        assert h == amodel.block_hash(parent, toks.tolist(), extra)
+        parent = h
+
+
+def test_block_hash_is_chained_and_salted():
+    """A hash names a prefix ending at a boundary: the same sixteen tokens
+    after different parents hash differently; the salt reaches every later
+    block through the chain."""
+    a = np.arange(B, dtype=np.int32)
+    b = np.arange(100, 100 + B, dtype=np.int32)
+    h_a = pkv.hash_block_tokens(None, a)
+    h_b = pkv.hash_block_tokens(None, b)
+    assert pkv.hash_block_tokens(h_a, a) != pkv.hash_block_tokens(h_b, a)
+    assert pkv.hash_block_tokens(h_a, a) == pkv.hash_block_tokens(pkv.hash_block_tokens(None, a), a)
+    assert pkv.hash_block_tokens(None, a, 7) != h_a
+    assert pkv.hash_block_tokens(pkv.hash_block_tokens(None, a, 7), b) != pkv.hash_block_tokens(h_a, b)
+
+
+# --------------------------------------------------------------- policy pins
+def both(nb):
+    c, m = pkv.Allocator(nb), amodel.AllocatorModel(nb)
+    c.enable_prefix_caching()
+    m.enable_caching()
+    return c, m
+
+
+def fill(alloc, sid, tokens, is_model):
+    """Append and record a prompt the way a step would: blocks first, ids
+    after the K/V are written."""
+    if is_model:
+        alloc.append(sid, len(tokens) - alloc.length[sid])
+        st = alloc.chain[sid]
+        alloc.record_tokens(sid, tokens[st["recorded"]:])
+    else:
+        n_have = alloc.seq_len(sid)
+        alloc.append(sid, len(tokens) - n_have)
+        alloc.record_tokens(sid, tokens[n_have:])
+
+
+@pytest.mark.parametrize("impl", ["cpp", "model"])
+def test_freed_blocks_stay_cached_until_reused(impl):
+    """Freed blocks keep their hash and a new request with the same prompt
+    takes them back (same ids, out of the free queue); a partial last block
+    is never cached."""
+    c, m = both(16)
+    a = c if impl == "cpp" else m
+    is_m = impl == "model"
+    prompt = list(range(1000, 1000 + 3 * B + 5))            # 3 full blocks + 5 tokens
+    got = a.add_cached(1, prompt)
+    assert got == 0
+    fill(a, 1, prompt, is_m)
+    blocks = list(a.blocks[1]) if is_m else a.block_table([1], 4)[0][0].tolist()
+    free_before = a.num_free()
+    a.free_seq(1) if is_m else a.free(1)
+    assert a.num_free() == free_before + 4
+    got = a.add_cached(2, prompt)
+    assert got == 3 * B
+    now = list(a.blocks[2]) if is_m else a.block_table([2], 3)[0][0].tolist()
+    assert now == blocks[:3]
+    assert a.num_free() == free_before + 1                   # the 3 cached blocks left the queue
+    for b in blocks[:3]:
+        assert (a.ref[b] if is_m else a.refcount(b)) == 1
+
+
+@pytest.mark.parametrize("impl", ["cpp", "model"])
+def test_tail_evicted_first_and_lazily(impl):
+    """Hashed blocks go to the back of the free queue tail first; unhashed
+    ones to the front. Eviction happens only when the queue hands a block
+    out, tail first, so the cached prefix survives longest."""
+    c, m = both(5)                                           # 4 usable blocks
+    a = c if impl == "cpp" else m
+    is_m = impl == "model"
+    prompt = list(range(3 * B))
+    a.add_cached(1, prompt)
+    fill(a, 1, prompt, is_m)
+    a.free_seq(1) if is_m else a.free(1)                     # queue: [unhashed, t3, t2, t1]
+    st = a.cache_stats() if is_m else a.prefix_cache_stats()
+    assert st["cached_blocks"] == 3
+    a.add(9)
+    a.append(9, 2 * B)                                       # takes the unhashed block, then t3
+    st = a.cache_stats() if is_m else a.prefix_cache_stats()
+    assert st["cached_blocks"] == 2                          # t3 evicted now, not at free time
+    assert a.add_cached(2, prompt) == 2 * B                  # the first two blocks still hit
+
+
+@pytest.mark.parametrize("impl", ["cpp", "model"])
+def test_salt_separates_tenants(impl):
+    c, m = both(16)
+    a = c if impl == "cpp" else m
+    is_m = impl == "model"
+    prompt = list(range(2 * B))
+    a.add_cached(1, prompt, 11)
+    fill(a, 1, prompt, is_m)
+    assert a.add_cached(2, prompt, 12) == 0
+    assert a.add_cached(3, prompt, 0) == 0
+    assert a.add_cached(4, prompt, 11) == 2 * B
+
+
+@pytest.mark.parametrize("impl", ["cpp", "model"])
+def test_lookup_limit_and_disabled_cache(impl):
+    c, m = both(16)
+    a = c if impl == "cpp" else m
+    is_m = impl == "model"
+    prompt = list(range(4 * B))
+    a.add_cached(1, prompt)
+    fill(a, 1, prompt, is_m)
+    # a request whose whole prompt is cached may keep its last token to
+    # compute: the limit rounds down to full blocks
+    assert a.add_cached(2, prompt, 0, 4 * B - 1) == 3 * B
+    a2 = pkv.Allocator(16) if impl == "cpp" else amodel.AllocatorModel(16)
+    a2.add_cached(1, prompt)
+    fill(a2, 1, prompt, is_m)
+    assert a2.add_cached(2, prompt) == 0                     # caching off: no hits
+    assert (a2.block_hash_of(a2.blocks[1][0]) if is_m else a2.block_hash(1)) is None
+
+
+def test_switching_needs_an_empty_allocator():
+    c = pkv.Allocator(8)
+    c.add(1)
+    with pytest.raises(pkv.Error):
+        c.enable_prefix_caching()
+    m = amodel.AllocatorModel(8)
+    m.add(1)
+    with pytest.raises(ValueError):
+        m.enable_caching()
+
+
+def test_record_beyond_length_is_refused():
+    c, m = both(8)
+    c.add(1)
+    c.append(1, 5)
+    with pytest.raises(pkv.Error):
+        c.record_tokens(1, list(range(6)))
+    c.record_tokens(1, list(range(5)))                       # nothing changed by the refusal
+    m.add(1)
+    m.append(1, 5)
+    with pytest.raises(ValueError):
+        m.record_tokens(1, list(range(6)))
+
+
+# ------------------------------------------------------- C++ against model
+def _state_equal(c, m, live):
+    assert c.num_free() == m.num_free()
+    for b in range(m.num_blocks):
+        assert c.refcount(b) == (0 if b == 0 else m.ref[b]), b
+        assert c.block_hash(b) == m.block_hash_of(b), b
+    assert c.prefix_cache_stats() == m.cache_stats()
+    if live:
+        maxb = max(1, max(len(m.blocks[s]) for s in live))
+        t1, l1 = c.block_table(live, maxb)
+        t2, l2 = m.block_table(live, maxb)
+        assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+
+
+def _fuzz(seed):
+    rng = np.random.default_rng(seed)
+    nb = int(rng.integers(12, 60))
+    c, m = both(nb)
+    if seed % 2:
+        order = rng.permutation(np.arange(1, nb)).astype(np.int32)
+        c.set_free_order(order)
+        m.set_free_order(order.tolist())
+    # prompts built from a few shared stems, so lookups hit, miss and stop
+    stems = [rng.integers(0, 50, int(rng.integers(1, 5)) * B).tolist() for _ in range(4)]
+    live, prompts, nxt = [], {}, 1
+    for step in range(250):
+        op = rng.integers(0, 6)
+        if op <= 1 or not live:
+            stem = stems[int(rng.integers(0, len(stems)))]
+            cut = int(rng.integers(0, len(stem) + 1))
+            prompt = stem[:cut] + rng.integers(0, 50, int(rng.integers(0, 40))).tolist()
+            salt = 0 if rng.random() < 0.85 else 1
+            lim = -1 if rng.random() < 0.7 else int(rng.integers(0, len(prompt) + 1))
+            got_c = c.add_cached(nxt, prompt, salt, lim)
+            got_m = m.add_cached(nxt, prompt, salt, lim)
+            assert got_c == got_m
+            live.append(nxt)
+            prompts[nxt] = prompt
+            nxt += 1
+        elif op == 2:
+            # schedule the rest of a prompt (or some generated tokens)
+            sid = int(rng.choice(live))
+            have = m.length[sid]
+            want = len(prompts[sid]) - have
+            n = want if want > 0 else int(rng.integers(1, 20))
+            try:
+                s2, p2 = m.append(sid, n)
+            except amodel.OutOfBlocks:
+                with pytest.raises(pkv.Error):
+                    c.append(sid, n)
+                continue
+            s1, p1 = c.append(sid, n)
+            assert s1.tolist() == s2 and p1 == p2
+            if want <= 0:
+                prompts[sid] = prompts[sid] + rng.integers(0, 50, n).tolist()
+            if rng.random() < 0.6:
+                # the step ran: record the ids of the appended tokens now
+                ids = prompts[sid][m.chain[sid]["recorded"]:m.length[sid]]
+                c.record_tokens(sid, ids)
+                m.record_tokens(sid, ids)
+        elif op == 3:
+            # the step ran: record ids of everything appended so far
+            sid = int(rng.choice(live))
+            st = m.chain[sid]
+            ids = prompts[sid][st["recorded"]:m.length[sid]]
+            c.record_tokens(sid, ids)
+            m.record_tokens(sid, ids)
+        elif op == 4:
+            parent = int(rng.choice(live))
+            c.fork(parent, nxt)
+            m.fork(parent, nxt)
+            live.append(nxt)
+            prompts[nxt] = list(prompts[parent])
+            nxt += 1
+        else:
+            sid = int(rng.choice(live))
+            c.free(sid)
+            m.free_seq(sid)
+            live.remove(sid)
+        _state_equal(c, m, live)
+    return m.cache_stats()["hit_blocks"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cpp_matches_model_with_caching(seed):
+    _fuzz(seed)
+
+
+def test_fuzz_reaches_cache_hits():
+    """The random streams do exercise hits (not only misses)."""
+    assert sum(_fuzz(s) for s in range(4)) > 0
