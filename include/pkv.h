@@ -291,6 +291,37 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
                                      float scale, int32_t dtype, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Workspace bytes pkv_paged_attention_decode_shared_prefix needs for these
+ * sizes on the current device. */
+int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t prefix_blocks, size_t* out);
+
+/* Decode attention for a batch whose sequences all start with the same
+ * prefix_blocks physical blocks (a shared prefix held once, refcounted
+ * ["(2) vLLM Internals ...", 1.2 "Three Direct Wins", items 2 and 3;
+ * "vLLM: what PagedAttention turned into", "The block pool, and the two
+ * tricks in it"]). Same result as pkv_paged_attention_decode (to rounding),
+ * computed as: every query against the shared prefix at once, as dense MFMA
+ * tiles over all sequences' query rows (the prefix is read once per KV head
+ * instead of once per sequence), then each sequence's own blocks, whose
+ * softmax state starts from the prefix's. The prefix block ids are read
+ * from row 0 of block_table; every sequence's context_lens must be at least
+ * prefix_blocks*16 and its first prefix_blocks table entries equal row 0's
+ * (caller contract; otherwise the result is undefined but every access stays
+ * inside the pools and the table). fp32 and prefix_blocks == 0 run the
+ * ordinary decode. workspace: >= pkv_decode_shared_prefix_workspace_size
+ * bytes, device memory, no initialisation. Other arguments as
+ * pkv_paged_attention_decode. */
+int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_table,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                                             int32_t prefix_blocks, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, float scale,
+                                             int32_t dtype, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attention_prefill_chunk needs (0 if none). */
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,

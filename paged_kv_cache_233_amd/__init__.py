@@ -75,6 +75,12 @@ _SIGNATURES = {
     "pkv_reshape_and_cache": ([_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_p], ctypes.c_int),
     "pkv_stage_copy": ([_c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
+    "pkv_decode_shared_prefix_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p],
+                                                ctypes.c_int),
+    "pkv_paged_attention_decode_shared_prefix": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t, _c_p],
+                                                ctypes.c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p],
                         ctypes.c_int),
     "pkv_decode_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)],
@@ -428,6 +434,42 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
         _idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32),
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_shared_prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                        head_dim: int, prefix_blocks: int) -> int:
+    out = _c_sz(0)
+    _check(library().pkv_decode_shared_prefix_workspace_size(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(prefix_blocks),
+        ctypes.byref(out)))
+    return out.value
+
+
+def decode_shared_prefix(out, q, k_cache, v_cache, block_table, context_lens, prefix_blocks: int,
+                         scale: float, workspace=None, stream=None) -> None:
+    """Decode for a batch sharing its first prefix_blocks blocks (row 0 of
+    block_table holds them): the prefix is attended once for all sequences,
+    then each sequence's own blocks. workspace: uint8 device tensor of at
+    least decode_shared_prefix_workspace_size(...) bytes (allocated here if
+    None)."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
+        raise Error(ERR_INVALID_ARG, "q/out must be [S, Hq, %d]" % d)
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    s, hq = int(q.shape[0]), int(q.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != s or context_lens.numel() != s:
+        raise Error(ERR_INVALID_ARG, "block_table must be [S, maxB] and context_lens [S]")
+    if workspace is None:
+        workspace = torch.empty(max(1, decode_shared_prefix_workspace_size(s, hq, hkv, d, prefix_blocks)),
+                                dtype=torch.uint8, device=q.device)
+    _check(library().pkv_paged_attention_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32),
+        s, nb, int(block_table.shape[1]), int(prefix_blocks), hq, hkv, d, float(scale),
+        _dtype_code(q), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def prefill_workspace_size(num_chunks: int, total_q: int, num_q_heads: int, num_kv_heads: int,

@@ -203,6 +203,81 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
                       workspace, workspace_bytes, stream, 2);
 }
 
+// Workspace of the shared-prefix decode: the decode workspace, then the
+// prefix states (parts x num_seqs x num_q_heads x (head_dim + 4) floats).
+static size_t shared_prefix_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t prefix_blocks, int32_t* parts) {
+  const size_t dec = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
+                      255) / 256 * 256;
+  *parts = pkv::prefix_state_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks * 16);
+  return dec + (size_t)*parts * num_seqs * num_q_heads * (head_dim + 4) * 4;
+}
+
+int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t prefix_blocks, size_t* out) {
+  pkv::clear_error();
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  if (num_seqs < 0 || prefix_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
+  int32_t parts;
+  *out = shared_prefix_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_blocks, &parts);
+  return PKV_OK;
+}
+
+int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                             const void* v_cache, const int32_t* block_table,
+                                             const int32_t* context_lens, int32_t num_seqs,
+                                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                                             int32_t prefix_blocks, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, float scale,
+                                             int32_t dtype, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  pkv::clear_error();
+  if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+    return fail(PKV_ERR_INVALID_ARG, "prefix_blocks %d outside [0, max_blocks_per_seq %d]",
+                prefix_blocks, max_blocks_per_seq);
+  // fp32 (no bf16 MFMA prefix phase) and an empty prefix: the ordinary decode
+  if (prefix_blocks == 0 || dtype == PKV_F32)
+    return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                        workspace, workspace_bytes, stream, 3);
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (num_seqs < 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || !block_table)
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 1) > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs*num_kv_heads*max_blocks_per_seq too large");
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache |
+       (uintptr_t)workspace) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "q, out, pools and workspace must be 16-byte aligned");
+  if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
+  int32_t parts;
+  const size_t need = shared_prefix_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          prefix_blocks, &parts);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "shared-prefix decode needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const size_t dec = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
+                      255) / 256 * 256;
+  float* state = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec);
+  pkv::PrefillArgs pa{nullptr, q, nullptr, nullptr, block_table, k_cache, v_cache, 1, num_seqs,
+                      num_blocks, max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads,
+                      head_dim, scale, dtype};
+  hipError_t err = pkv::launch_prefix_state(pa, prefix_blocks * 16, parts, state,
+                                            (hipStream_t)stream);
+  if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix phase launch");
+  pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                    max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                    workspace};
+  err = pkv::launch_decode_after_prefix(a, prefix_blocks, state, parts, 3, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
+}
+
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
                                int32_t max_context_len, size_t* out) {

@@ -56,6 +56,15 @@ struct DecodeParams {
   int32_t num_waves;
   int32_t pieces_per_round;  // pieces whose query rows fit the LDS budget
   float scale_log2;
+  // Shared-prefix mode: every sequence's first `skip` blocks were attended
+  // by the prefix phase, whose `pparts` softmax states per query row
+  // (pstate[part * pstride + row * (D + 4)]: O[D], max (log2 units), sum, two
+  // floats of padding that keep every row 16-byte aligned)
+  // start the sequence's state. skip = 0 and pstate = nullptr otherwise.
+  int32_t skip;
+  int32_t pparts;
+  const float* pstate;
+  int64_t pstride;
 };
 
 // Length of sequence s after clamping to [0, table width in tokens]; s may
@@ -64,7 +73,9 @@ __device__ __forceinline__ int32_t seq_len_clamped(const DecodeParams& p, int32_
   int32_t n = p.context_lens[s];
   n = n < 0 ? 0 : n;
   const int32_t cap = p.max_blocks * 16;
-  return n > cap ? cap : n;
+  n = n > cap ? cap : n;
+  n -= 16 * p.skip;                      // positions left after the shared prefix
+  return n < 0 ? 0 : n;
 }
 
 // The same for a wave-uniform s, kept in a scalar register.
@@ -111,6 +122,66 @@ __device__ __forceinline__ int32_t wave_of(int64_t i, int64_t total, int32_t W) 
 
 __device__ __forceinline__ bool wave_empty(int32_t w, int64_t total, int32_t W) {
   return total * w / W == total * (w + 1) / W;
+}
+
+// Softmax state of query row `row` folded from the prefix states: lane
+// (n, kg) of the tile layout gets dims (4kg + i) * (D/16) + e.
+template <int DT, int D>
+__device__ __forceinline__ void prefix_init(const DecodeParams& p, State<DT, D>& st, int64_t row,
+                                            int kg) {
+  using Sh = Shape<DT, D>;
+  float m = -INFINITY;
+  for (int32_t k = 0; k < p.pparts; ++k) m = fmaxf(m, p.pstate[k * p.pstride + row * (D + 4) + D]);
+  st.m = m;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < Sh::kTiles; ++e) st.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t k = 0; k < p.pparts; ++k) {
+    const float* src = p.pstate + k * p.pstride + row * (D + 4);
+    const float wk = __builtin_amdgcn_exp2f(src[D] - m);
+    st.l += src[D + 1] * wk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* od = src + (4 * kg + i) * Sh::kTiles;
+#pragma unroll
+      for (int e = 0; e < Sh::kTiles; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(od + e);
+        st.o[e][i] += v.x * wk;
+        st.o[e + 1][i] += v.y * wk;
+        st.o[e + 2][i] += v.z * wk;
+        st.o[e + 3][i] += v.w * wk;
+      }
+    }
+  }
+}
+
+// Output of a sequence with nothing after the shared prefix: its prefix
+// states folded and normalised (all query heads).
+template <int DT, int D>
+__device__ __forceinline__ void prefix_rows(const DecodeParams& p, int32_t s) {
+  for (int32_t h = 0; h < p.num_q_heads; ++h) {
+    const int64_t row = (int64_t)s * p.num_q_heads + h;
+    float m = -INFINITY;
+    for (int32_t k = 0; k < p.pparts; ++k) m = fmaxf(m, p.pstate[k * p.pstride + row * (D + 4) + D]);
+    float l = 0.f;
+    for (int32_t k = 0; k < p.pparts; ++k) {
+      const float* src = p.pstate + k * p.pstride + row * (D + 4);
+      l += src[D + 1] * __builtin_amdgcn_exp2f(src[D] - m);
+    }
+    for (int32_t d = threadIdx.x; d < D; d += 64) {
+      float o = 0.f;
+      for (int32_t k = 0; k < p.pparts; ++k) {
+        const float* src = p.pstate + k * p.pstride + row * (D + 4);
+        o += src[d] * __builtin_amdgcn_exp2f(src[D] - m);
+      }
+      o /= l;
+      if constexpr (DT == PKV_BF16) {
+        reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)o;
+      } else {
+        reinterpret_cast<float*>(p.out)[row * D + d] = o;
+      }
+    }
+  }
 }
 
 // Zero output of an empty sequence (all query heads).
@@ -260,7 +331,10 @@ decode_split_kernel(DecodeParams p) {
       while (empty) {
         const int li = __builtin_ctzll(empty);
         empty &= empty - 1;
-        zero_rows<DT, D>(p, base + li);
+        if (p.pstate != nullptr)
+          prefix_rows<DT, D>(p, base + li);
+        else
+          zero_rows<DT, D>(p, base + li);
       }
     }
     per_head += __builtin_amdgcn_readlane(incl, 63);
@@ -335,7 +409,7 @@ decode_split_kernel(DecodeParams p) {
         // (contiguous, at most 8 KiB): all loads of a 64-tile chunk are
         // issued before anything is written, so one memory round trip
         // stages them.
-        const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks + j;
+        const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks + p.skip + j;
         const char* qsrc = reinterpret_cast<const char*>(p.q) +
                            ((int64_t)s * p.num_q_heads + (int64_t)g * G) * Sh::kRow;
         char* qdst = qlds + np * qbytes;
@@ -404,6 +478,10 @@ decode_split_kernel(DecodeParams p) {
             qv[0].c[c] = n < G ? *reinterpret_cast<const uint4*>(qrow + 64 * c + 16 * kg)
                                : uint4{0u, 0u, 0u, 0u};
           st[0].reset();
+          // the sequence's first tile after a shared prefix: start from the
+          // prefix states (once per sequence and KV head)
+          if (p.pstate != nullptr && j0 == 0 && n < G)
+            prefix_init<DT, D>(p, st[0], (int64_t)ps * p.num_q_heads + pg * G + n, kg);
         }
       }
       const int32_t t0 = 16 * (j0 + k - kstart);
@@ -547,8 +625,13 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return prefix + partial;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
+static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const float* pstate,
+                                     int32_t pparts, int phases, hipStream_t stream) {
   DecodeParams p;
+  p.skip = skip;
+  p.pstate = pstate;
+  p.pparts = pparts;
+  p.pstride = (int64_t)a.num_seqs * a.num_q_heads * (a.head_dim + 4);
   p.out = a.out;
   p.q = a.q;
   p.k_cache = reinterpret_cast<const char*>(a.k_cache);
@@ -578,6 +661,16 @@ hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
   }
   return a.head_dim == 128 ? launch<PKV_F32, 128>(p, phases, stream)
                            : launch<PKV_F32, 64>(p, phases, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
+  return launch_decode_impl(a, 0, nullptr, 0, phases, stream);
+}
+
+hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
+                                      const float* prefix_state, int32_t parts, int phases,
+                                      hipStream_t stream) {
+  return launch_decode_impl(a, skip_blocks, prefix_state, parts, phases, stream);
 }
 
 }  // namespace pkv

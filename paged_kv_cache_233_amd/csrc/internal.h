@@ -65,6 +65,12 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
                               int32_t head_dim);
 // phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.
 hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream);
+// Decode over each sequence's blocks from `skip_blocks` on, starting every
+// sequence's softmax state from the `parts` prefix states (see
+// launch_prefix_state) instead of from nothing.
+hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
+                                      const float* prefix_state, int32_t parts, int phases,
+                                      hipStream_t stream);
 
 struct PrefillArgs {
   void* out;
@@ -87,5 +93,15 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Shared-prefix decode, first phase: the softmax states of every query
+// (total_q sequences' tokens) over positions [0, prefix_tokens) of
+// block_table row 0, split in `parts` position ranges; state[part][row][D+4]
+// holds unnormalised O, the reference max (log2 units), the sum and two
+// floats of padding (16-byte aligned rows). bf16 only.
+int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t prefix_tokens);
+hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int32_t parts,
+                               float* state, hipStream_t stream);
 
 }  // namespace pkv
