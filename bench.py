@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the leg that times the shared-prefix decode on the shared workload")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the leg that replays the whole step as one HIP graph")
     ap.add_argument("--stage", choices=["kernel", "dma", "mapped"], default="kernel",
@@ -169,36 +171,7 @@ def main():
     log("workload %s: %d decode seqs, pool %d blocks, max %d blocks/seq" % (w.name, S, nb, maxb))
 
     # ---------------------------------------------------------------- setup
-    alloc = pkv.Allocator(nb)
-    order = np.concatenate([w.free_order, np.arange(w.num_blocks, nb, dtype=np.int32)])
-    alloc.set_free_order(order)
-    shape = (nb, w.num_kv_heads, 16, w.head_dim)
-    kc0 = torch.zeros(shape, dtype=dt, device=dev)
-    vc0 = torch.zeros(shape, dtype=dt, device=dev)
-    specs = {s.seq_id: s for s in w.seqs}
-    cur = {}
-    kvcache = {}
-    for op in w.setup_ops():
-        if op[0] == "add":
-            alloc.add(op[1])
-            cur[op[1]] = 0
-        elif op[0] == "fork":
-            alloc.fork(op[1], op[2])
-            cur[op[2]] = cur[op[1]]
-        else:
-            sid, n = op[1], op[2]
-            slots, pairs = alloc.append(sid, n)
-            if pairs:
-                pkv.copy_blocks(kc0, vc0, torch.tensor(pairs, dtype=torch.int64, device=dev))
-            if sid not in kvcache:
-                kvcache[sid] = w.seq_kv(specs[sid])
-            k, v = kvcache[sid]
-            p0 = cur[sid]
-            pkv.reshape_and_cache(kc0, vc0, k[p0:p0 + n].to(dev), v[p0:p0 + n].to(dev),
-                                  torch.from_numpy(slots).to(dev))
-            cur[sid] = p0 + n
-    kvcache.clear()
-    torch.cuda.synchronize()
+    alloc, kc0, vc0 = build_pool(w, dev, nb)
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.pools - 1)]
     sids = np.array([s.seq_id for s in dec], dtype=np.int64)
     ones = np.ones(S, dtype=np.int32)
@@ -343,6 +316,7 @@ def main():
                                                             graph["value"]))
 
     prefill = None if args.no_prefill else prefill_leg(args, dev)
+    shared = None if args.no_shared else shared_leg(args, dev)
 
     # ------------------------------------------------------- CPU oracle leg
     cpu = None
@@ -385,9 +359,119 @@ def main():
                       "frac_of_hbm_peak": round(achieved_op / HBM_PEAK_GBS, 4)},
         "graph_step": graph,
         "prefill": prefill,
+        "shared_prefix": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def build_pool(w, dev, nb, step=False):
+    """Allocator and K/V pools of a workload's cached tokens (pool of nb
+    blocks, the workload's random placement first); with step=True also the
+    step's new tokens. K/V are the workload's seeded values, written through
+    reshape_and_cache (copy-on-write pairs through copy_blocks)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+
+    alloc = pkv.Allocator(nb)
+    order = np.concatenate([w.free_order, np.arange(w.num_blocks, nb, dtype=np.int32)])
+    alloc.set_free_order(order)
+    shape = (nb, w.num_kv_heads, 16, w.head_dim)
+    kc = torch.zeros(shape, dtype=w.torch_dtype, device=dev)
+    vc = torch.zeros(shape, dtype=w.torch_dtype, device=dev)
+    specs = {s.seq_id: s for s in w.seqs}
+    cur = {}
+    kvcache = {}
+    ops = list(w.setup_ops())
+    if step:
+        ops += [("append", sid, n) for sid, n in zip(*w.step_appends())]
+    for op in ops:
+        if op[0] == "add":
+            alloc.add(op[1])
+            cur[op[1]] = 0
+        elif op[0] == "fork":
+            alloc.fork(op[1], op[2])
+            cur[op[2]] = cur[op[1]]
+        else:
+            sid, n = op[1], op[2]
+            slots, pairs = alloc.append(sid, n)
+            if pairs:
+                pkv.copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device=dev))
+            if sid not in kvcache:
+                kvcache[sid] = w.seq_kv(specs[sid])
+            k, v = kvcache[sid]
+            p0 = cur[sid]
+            pkv.reshape_and_cache(kc, vc, k[p0:p0 + n].to(dev), v[p0:p0 + n].to(dev),
+                                  torch.from_numpy(slots).to(dev))
+            cur[sid] = p0 + n
+    torch.cuda.synchronize()
+    return alloc, kc, vc
+
+
+def shared_leg(args, dev):
+    """The shared workload (128 sequences whose first 2048 tokens are the same
+    128 physical blocks) decoded two ways: the ordinary decode (every
+    sequence reads the prefix through its table) and the shared-prefix
+    decode (the prefix attended once for all sequences as MFMA tiles, then
+    each sequence's own blocks). Reports kernel time and GB/s on logical
+    bytes (every attended token's K/V once per sequence) and on unique bytes
+    (each physical block once)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    w = workloads.named("shared")
+    dec = w.decode_seqs
+    S = len(dec)
+    alloc, kc, vc = build_pool(w, dev, w.num_blocks, step=True)
+    sids = [s.seq_id for s in dec]
+    maxb = w.max_blocks_per_seq()
+    table, lens = alloc.block_table(sids, maxb)
+    prefix_blocks = 128
+    assert (table[:, :prefix_blocks] == table[0, :prefix_blocks]).all()
+    d_table, d_lens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    gen = torch.Generator().manual_seed(4321)
+    q = torch.randn((S, w.num_q_heads, w.head_dim), generator=gen).to(w.torch_dtype).to(dev)
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
+    wsp = torch.empty(pkv.decode_shared_prefix_workspace_size(S, w.num_q_heads, w.num_kv_heads,
+                                                              w.head_dim, prefix_blocks),
+                      dtype=torch.uint8, device=dev)
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    reps = max(20, args.steps // 2)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        e0, e1 = hip.create(), hip.create()
+        hip.record(e0, sh)
+        for _ in range(reps):
+            fn()
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        return hip.elapsed_us(e0, e1) / reps
+
+    plain = timed(lambda: pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws))
+    shared = timed(lambda: pkv.decode_shared_prefix(out, q, kc, vc, d_table, d_lens, prefix_blocks,
+                                                    w.scale, wsp))
+    per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    logical = float(lens.sum()) * per_token
+    unique = float(prefix_blocks * 16 + (lens - prefix_blocks * 16).sum()) * per_token
+    log("shared prefix: ordinary decode %.1f us, shared-prefix decode %.1f us (x%.2f)"
+        % (plain, shared, plain / shared))
+    return {"workload": "shared: 128 seqs, one 2048-token prefix held once (128 blocks, refcount 128) "
+                        "+ private suffixes U[16,512], 32 q / 8 kv heads, head_dim 128, bf16",
+            "logical_kv_bytes": int(logical), "unique_kv_bytes": int(unique),
+            "ordinary_decode_us": round(plain, 2), "shared_prefix_decode_us": round(shared, 2),
+            "speedup": round(plain / shared, 3),
+            "ordinary_logical_gbs": round(logical / plain / 1e3, 1),
+            "shared_prefix_logical_gbs": round(logical / shared / 1e3, 1),
+            "shared_prefix_unique_gbs": round(unique / shared / 1e3, 1)}
 
 
 def prefill_leg(args, dev):
