@@ -62,6 +62,8 @@ def parse():
                          "pinned host memory")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--shared-probe", action="store_true",
+                    help="only run the shared-prefix leg and print its JSON (for profiling it alone)")
     return ap.parse_args()
 
 
@@ -161,6 +163,9 @@ def main():
         return
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.shared_probe:
+        print(json.dumps({"shared_prefix": shared_leg(args, dev)}), flush=True)
+        return
     w = workloads.named(args.config)
     dec = w.decode_seqs
     S = len(dec)
