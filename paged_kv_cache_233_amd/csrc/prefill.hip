@@ -825,21 +825,27 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream) : launch<PKV_F32, 64>(p, stream);
 }
 
+constexpr int kMaxPrefixParts = 16;
+
 int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t prefix_tokens) {
-  // Enough workgroups for two per CU: (row blocks x KV heads) x parts, each
-  // part keeping at least two 32-position tiles.
+  // About one workgroup per CU: (row blocks x KV heads) x parts, each part
+  // keeping at least two 32-position tiles. With fewer workgroups than two
+  // per CU each runs eight waves over two halves of its positions, which
+  // keeps the per-wave work of 2x the parts while writing half the partial
+  // states (measured on the shared workload: 8 parts 15.2 + 5.0 us for the
+  // prefix and its fold, 16 parts 16.8 + 7.4 us).
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t wg_tokens = kWaves * 2 * (16 / group);
   const int64_t base = (int64_t)((num_seqs + wg_tokens - 1) / wg_tokens) * num_kv_heads;
   const int32_t tiles = (prefix_tokens + kKeys - 1) / kKeys;
-  int64_t parts = (2 * (int64_t)num_cus() + base - 1) / base;
+  int64_t parts = ((int64_t)num_cus() + base - 1) / base;
   parts = std::min<int64_t>(parts, std::max<int32_t>(1, tiles / 2));
   if (const char* env = getenv("PKV_PREFIX_PARTS")) {  // tuning override
     const int v = atoi(env);
-    if (v >= 1 && v <= 16) parts = v;
+    if (v >= 1 && v <= kMaxPrefixParts) parts = v;
   }
-  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, 16));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kMaxPrefixParts));
 }
 
 hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int32_t parts,
@@ -868,6 +874,72 @@ hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int3
   p.state_part_stride = (int64_t)a.total_q * a.num_q_heads * (a.head_dim + 4);
   if (a.dtype != PKV_BF16) return hipErrorInvalidValue;
   return a.head_dim == 128 ? launch_lds<128, 2>(p, stream) : launch_lds<64, 2>(p, stream);
+}
+
+namespace {
+
+// One softmax state per query row from the prefix's per-part states: with
+// M = max_k m_k and w_k = 2^(m_k - M), the sum is sum_k w_k l_k and the
+// unnormalised output sum_k w_k O_k (the same rescaling the online softmax
+// applies when it moves its reference). D/4 lanes per row, four dims each;
+// every part's loads are issued before any is used.
+template <int D>
+__global__ void __launch_bounds__(256)
+prefix_fold_kernel(const float* __restrict__ state, int64_t part_stride, int32_t parts, int64_t rows,
+                   float* __restrict__ folded) {
+  constexpr int kLanes = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / kLanes;
+  const int c = (int)(t % kLanes);
+  if (row >= rows) return;
+  const float* src = state + row * (D + 4);
+  float4 o[kMaxPrefixParts];
+  float2 ml[kMaxPrefixParts];
+#pragma unroll
+  for (int k = 0; k < kMaxPrefixParts; ++k) {
+    if (k < parts) {
+      o[k] = *reinterpret_cast<const float4*>(src + k * part_stride + 4 * c);
+      ml[k] = *reinterpret_cast<const float2*>(src + k * part_stride + D);
+    }
+  }
+  float m = ml[0].x;
+#pragma unroll
+  for (int k = 1; k < kMaxPrefixParts; ++k)
+    if (k < parts) m = fmaxf(m, ml[k].x);
+  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPrefixParts; ++k) {
+    if (k < parts) {
+      const float w = __builtin_amdgcn_exp2f(ml[k].x - m);
+      acc.x += o[k].x * w;
+      acc.y += o[k].y * w;
+      acc.z += o[k].z * w;
+      acc.w += o[k].w * w;
+      l += ml[k].y * w;
+    }
+  }
+  float* dst = folded + row * (D + 4);
+  *reinterpret_cast<float4*>(dst + 4 * c) = acc;
+  if (c == 0) *reinterpret_cast<float4*>(dst + D) = float4{m, l, 0.f, 0.f};
+}
+
+}  // namespace
+
+hipError_t launch_prefix_fold(const float* state, int32_t parts, int64_t rows, int32_t head_dim,
+                              float* folded, hipStream_t stream) {
+  if (parts < 1 || parts > kMaxPrefixParts || (head_dim != 64 && head_dim != 128))
+    return hipErrorInvalidValue;
+  const int64_t threads = rows * (head_dim / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t stride = rows * (head_dim + 4);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(prefix_fold_kernel<128>, grid, dim3(256), 0, stream, state, stride, parts, rows,
+                       folded);
+  else
+    hipLaunchKernelGGL(prefix_fold_kernel<64>, grid, dim3(256), 0, stream, state, stride, parts, rows,
+                       folded);
+  return hipGetLastError();
 }
 
 }  // namespace pkv
