@@ -142,6 +142,13 @@ int pkv_seq_free(pkv_allocator* a, int64_t seq_id);
 /* Switch prefix caching on (enabled != 0) or off; only while no sequence
  * exists. Either way the map is emptied. */
 int pkv_allocator_enable_prefix_caching(pkv_allocator* a, int32_t enabled);
+/* What pkv_seq_add_cached would attach for this prompt, without changing
+ * anything: *out_cached_tokens (a multiple of 16) and *out_revived_blocks,
+ * how many of those blocks are free now and would leave the free queue.
+ * A scheduler uses it to check that a prompt fits before admitting it. */
+int pkv_prefix_lookup(pkv_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                      uint64_t extra_key, int32_t max_cached_tokens, int32_t* out_cached_tokens,
+                      int32_t* out_revived_blocks);
 /* Create a sequence for a prompt of n_tokens token ids and attach the
  * longest run of cached full blocks from its start (at most
  * max_cached_tokens tokens; < 0 means no limit), walking block by block and
@@ -195,6 +202,69 @@ int pkv_allocator_stats(pkv_allocator* a, pkv_stats* out);
  * what PagedAttention turned into", section "Checking the 96.3%"]. */
 int pkv_blocks_for_bytes(int64_t bytes, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                          int32_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* Step scheduler (host, C++) over an allocator.
+ * Iteration-level scheduling with one token budget per step and no prefill
+ * or decode phase: each request has the tokens it holds (prompt, then
+ * generated tokens) and the count whose K/V are computed. A step walks the
+ * running requests first, in admission order, giving each
+ * min(tokens still to compute, budget left); then the waiting queue, each
+ * admitted prompt getting the same share, capped by long_prefill_threshold
+ * when it is > 0 (the cap applies to running requests too). A prompt cut by
+ * the budget continues next step (chunked prefill); with chunked_prefill ==
+ * 0 a prompt that does not fit stops the admission walk and waits
+ * ["vLLM: what PagedAttention turned into", "The scheduler, and what it has
+ * to balance now"; "(2) vLLM Internals ...", "2. Continuous Batching"].
+ * When the pool cannot hold a running request's tokens, the request admitted
+ * last is preempted: its blocks are freed, its computed count reset to 0 and
+ * it goes to the front of the waiting queue (recompute); a step that
+ * preempted admits no one ["vLLM: what PagedAttention turned into",
+ * "Preemption, and the path that got deleted"]. At admission the prompt's
+ * cached full blocks (prefix caching on the allocator) are attached and count
+ * as computed, at most all tokens but one. A step that completes a request's
+ * tokens samples one token (passed to pkv_scheduler_update), computed in a
+ * later step; a request finishes with max_new_tokens generated tokens and
+ * its blocks are freed. max_num_seqs > 0 bounds the running requests.
+ * Each request owns the allocator sequence with its id; the caller must not
+ * touch those sequences. The scheduler does not own the allocator, which
+ * must outlive it. Not thread-safe. */
+typedef struct pkv_scheduler pkv_scheduler;
+int pkv_scheduler_create(pkv_allocator* alloc, int32_t token_budget, int32_t long_prefill_threshold,
+                         int32_t chunked_prefill, int32_t max_num_seqs, pkv_scheduler** out);
+int pkv_scheduler_destroy(pkv_scheduler* s);
+/* Queue a request (prompt_len >= 1 token ids, copied). PKV_ERR_SEQ_EXISTS
+ * if the id was used before. */
+int pkv_scheduler_add_request(pkv_scheduler* s, int64_t req_id, const int32_t* prompt,
+                              int32_t prompt_len, int32_t max_new_tokens, uint64_t extra_key);
+/* Plan one step: sizes of the plan (outputs may be NULL). The allocator
+ * already holds the planned positions' slots when this returns. Must be
+ * followed by pkv_scheduler_update before the next call. */
+int pkv_scheduler_schedule(pkv_scheduler* s, int32_t* out_num_scheduled, int64_t* out_num_tokens,
+                           int32_t* out_num_preempted);
+/* Copy the plan out (each pointer may be NULL): per scheduled request, in
+ * plan order: id, first position computed this step, number of positions,
+ * whether the step samples a token for it (1/0); the slots of all planned
+ * positions in plan order (int64, out_num_tokens of them); the ids
+ * preempted this step. A request's context after the step is
+ * start + num_new tokens (its block table from pkv_fill_block_table). */
+int pkv_scheduler_plan(pkv_scheduler* s, int64_t* req_ids, int32_t* start_pos, int32_t* num_new,
+                       int32_t* samples, int64_t* slots, int64_t* preempted);
+/* The planned step ran (its K/V are in the pool): record the token ids of
+ * the computed positions (block hashes), advance the computed counts,
+ * append sampled[k] to the k-th sampling request in plan order, and free the
+ * requests that are now complete (*out_num_finished of them, ids from
+ * pkv_scheduler_finished). */
+int pkv_scheduler_update(pkv_scheduler* s, const int32_t* sampled, int32_t n_sampled,
+                         int32_t* out_num_finished);
+int pkv_scheduler_finished(pkv_scheduler* s, int64_t* req_ids);
+int pkv_scheduler_counts(pkv_scheduler* s, int32_t* num_waiting, int32_t* num_running);
+/* One request: state (0 waiting, 1 running, 2 finished), tokens held,
+ * computed count, times preempted, and (if tokens != NULL, max_tokens >=
+ * num_tokens) its token ids. Each output may be NULL. */
+int pkv_scheduler_request(pkv_scheduler* s, int64_t req_id, int32_t* state, int32_t* num_tokens,
+                          int32_t* computed, int32_t* preemptions, int32_t* tokens,
+                          int32_t max_tokens);
 
 /* ------------------------------------------------------------------------ */
 /* Device kernels (asynchronous on `stream`).

@@ -129,11 +129,9 @@ class AllocatorModel:
         self.length[sid] = 0
         self.chain[sid] = {"recorded": 0, "parent": None, "pending": [], "salt": 0}
 
-    def add_cached(self, sid: int, tokens: Sequence[int], salt: int = 0, max_cached: int = -1) -> int:
-        """New sequence for a prompt: attach the longest run of cached full
-        blocks from its start; returns the tokens attached."""
-        if sid in self.blocks:
-            raise KeyError("sequence exists")
+    def _walk_cached(self, tokens: Sequence[int], salt: int, max_cached: int):
+        """The cached blocks a prompt would attach, in order, and the hash of
+        the last one; changes nothing."""
         tokens = [int(t) for t in tokens]
         limit = len(tokens) if max_cached < 0 else min(len(tokens), max_cached)
         full = limit // BLOCK if self.caching else 0
@@ -144,11 +142,26 @@ class AllocatorModel:
             b = self.cache.get(h + GROUP_ID)
             if b is None:
                 break
+            got.append(b)
+            parent = h
+        return got, parent
+
+    def lookup_cached(self, tokens: Sequence[int], salt: int = 0, max_cached: int = -1):
+        """(tokens add_cached would attach, how many of those blocks it would
+        take back out of the free queue); changes nothing."""
+        got, _ = self._walk_cached(tokens, salt, max_cached)
+        return BLOCK * len(got), sum(1 for b in got if self.ref[b] == 0)
+
+    def add_cached(self, sid: int, tokens: Sequence[int], salt: int = 0, max_cached: int = -1) -> int:
+        """New sequence for a prompt: attach the longest run of cached full
+        blocks from its start; returns the tokens attached."""
+        if sid in self.blocks:
+            raise KeyError("sequence exists")
+        got, parent = self._walk_cached(tokens, salt, max_cached)
+        for b in got:
             if self.ref[b] == 0:
                 self.free.remove(b)
             self.ref[b] += 1
-            got.append(b)
-            parent = h
         self.blocks[sid] = got
         self.length[sid] = BLOCK * len(got)
         self.chain[sid] = {"recorded": BLOCK * len(got), "parent": parent, "pending": [],

@@ -174,3 +174,26 @@ def prefill_chunk(q, cu_q_lens, context_lens, k_pool, v_pool, block_table,
                 out[lo + i, heads] = _softmax_attend(qf[lo + i, heads], ks[g, :visible],
                                                      vs[g, :visible], scale)
     return out
+
+
+def attend_sequence(q, k, v, positions, scale: float) -> np.ndarray:
+    """Attention of one sequence's queries over its own tokens, no paging.
+
+    q is [m, Hq, D]; k and v are [n, Hkv, D], the sequence's tokens in
+    logical order; query i sits at positions[i] and attends to tokens
+    0 .. positions[i] (causal; decode is the case of one query at the last
+    position). This is what the paged kernels must return whatever the
+    placement of the blocks, the chunking of the prompt, preemption and
+    recompute, or prefix-cache reuse ("(2) vLLM Internals ...", section 1.1
+    "The Analogy": paging changes where K/V live, not what attention sees).
+    Returns float64 [m, Hq, D].
+    """
+    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
+    hq, hkv = qf.shape[1], kf.shape[1]
+    group = hq // hkv
+    out = np.zeros(qf.shape, dtype=np.float64)
+    for i, p in enumerate(positions):
+        for g in range(hkv):
+            heads = slice(g * group, (g + 1) * group)
+            out[i, heads] = _softmax_attend(qf[i, heads], kf[:p + 1, g], vf[:p + 1, g], scale)
+    return out

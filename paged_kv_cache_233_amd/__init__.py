@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, List, NamedTuple, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -62,6 +62,16 @@ _SIGNATURES = {
     "pkv_seq_len": ([_c_p, _c_i64, _c_p], ctypes.c_int),
     "pkv_allocator_enable_prefix_caching": ([_c_p, _c_i32], ctypes.c_int),
     "pkv_seq_add_cached": ([_c_p, _c_i64, _c_p, _c_i32, ctypes.c_uint64, _c_i32, _c_p], ctypes.c_int),
+    "pkv_prefix_lookup": ([_c_p, _c_p, _c_i32, ctypes.c_uint64, _c_i32, _c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_create": ([_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p], ctypes.c_int),
+    "pkv_scheduler_destroy": ([_c_p], ctypes.c_int),
+    "pkv_scheduler_add_request": ([_c_p, _c_i64, _c_p, _c_i32, _c_i32, ctypes.c_uint64], ctypes.c_int),
+    "pkv_scheduler_schedule": ([_c_p, _c_p, _c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_plan": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_update": ([_c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
+    "pkv_scheduler_finished": ([_c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_counts": ([_c_p, _c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_request": ([_c_p, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32], ctypes.c_int),
     "pkv_seq_record_tokens": ([_c_p, _c_i64, _c_p, _c_i32], ctypes.c_int),
     "pkv_block_hash": ([_c_p, _c_i32, _c_p, _c_p], ctypes.c_int),
     "pkv_prefix_cache_stats": ([_c_p, _c_p, _c_p, _c_p], ctypes.c_int),
@@ -210,6 +220,16 @@ class Allocator:
                                             ctypes.byref(got)))
         return int(got.value)
 
+    def lookup_cached(self, tokens, extra_key: int = 0, max_cached: int = -1):
+        """(tokens add_cached would attach, blocks it would take back out of
+        the free queue); changes nothing."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        got, rev = _c_i32(0), _c_i32(0)
+        _check(self._lib.pkv_prefix_lookup(self._h, _ptr(t) if t.size else None, int(t.size),
+                                           int(extra_key), int(max_cached), ctypes.byref(got),
+                                           ctypes.byref(rev)))
+        return int(got.value), int(rev.value)
+
     def record_tokens(self, sid: int, tokens) -> None:
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         _check(self._lib.pkv_seq_record_tokens(self._h, int(sid), _ptr(t) if t.size else None,
@@ -293,6 +313,93 @@ class Allocator:
         st = Stats()
         _check(self._lib.pkv_allocator_stats(self._h, ctypes.byref(st)))
         return {name: getattr(st, name) for name, _ in Stats._fields_}
+
+
+class StepPlan(NamedTuple):
+    """One planned step: per scheduled request (plan order) its id, first
+    position computed, number of positions and whether a token is sampled;
+    the slots of all planned positions in plan order; the ids preempted."""
+    req_ids: np.ndarray
+    start: np.ndarray
+    num_new: np.ndarray
+    samples: np.ndarray
+    slots: np.ndarray
+    preempted: np.ndarray
+
+
+class Scheduler:
+    """Step scheduler (C++) over an Allocator: one token budget per step,
+    running requests first, chunked prefill, preemption by recompute, prefix
+    cache lookups at admission when the allocator has caching on."""
+
+    WAITING, RUNNING, FINISHED = 0, 1, 2
+
+    def __init__(self, alloc: Allocator, token_budget: int, long_prefill_threshold: int = 0,
+                 chunked_prefill: bool = True, max_num_seqs: int = 0):
+        self._lib = library()
+        self.alloc = alloc                  # kept alive as long as the scheduler
+        h = _c_p()
+        _check(self._lib.pkv_scheduler_create(alloc._h, int(token_budget), int(long_prefill_threshold),
+                                              int(bool(chunked_prefill)), int(max_num_seqs),
+                                              ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pkv_scheduler_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, req_id: int, prompt, max_new_tokens: int, extra_key: int = 0) -> None:
+        t = np.ascontiguousarray(prompt, dtype=np.int32)
+        _check(self._lib.pkv_scheduler_add_request(self._h, int(req_id), _ptr(t) if t.size else None,
+                                                   int(t.size), int(max_new_tokens), int(extra_key)))
+
+    def schedule(self) -> StepPlan:
+        ns, nt, npre = _c_i32(0), _c_i64(0), _c_i32(0)
+        _check(self._lib.pkv_scheduler_schedule(self._h, ctypes.byref(ns), ctypes.byref(nt),
+                                                ctypes.byref(npre)))
+        n = ns.value
+        ids = np.empty(n, dtype=np.int64)
+        start = np.empty(n, dtype=np.int32)
+        num = np.empty(n, dtype=np.int32)
+        smp = np.empty(n, dtype=np.int32)
+        slots = np.empty(nt.value, dtype=np.int64)
+        pre = np.empty(npre.value, dtype=np.int64)
+        _check(self._lib.pkv_scheduler_plan(self._h, _ptr(ids), _ptr(start), _ptr(num), _ptr(smp),
+                                            _ptr(slots), _ptr(pre)))
+        return StepPlan(ids, start, num, smp.astype(bool), slots, pre)
+
+    def update(self, sampled) -> np.ndarray:
+        """The step ran; sampled holds one token per sampling request in plan
+        order. Returns the ids of the requests that finished."""
+        t = np.ascontiguousarray(sampled, dtype=np.int32)
+        nf = _c_i32(0)
+        _check(self._lib.pkv_scheduler_update(self._h, _ptr(t) if t.size else None, int(t.size),
+                                              ctypes.byref(nf)))
+        out = np.empty(nf.value, dtype=np.int64)
+        _check(self._lib.pkv_scheduler_finished(self._h, _ptr(out)))
+        return out
+
+    def counts(self) -> Tuple[int, int]:
+        w, r = _c_i32(0), _c_i32(0)
+        _check(self._lib.pkv_scheduler_counts(self._h, ctypes.byref(w), ctypes.byref(r)))
+        return w.value, r.value
+
+    def request(self, req_id: int) -> dict:
+        st, nt, comp, pre = _c_i32(0), _c_i32(0), _c_i32(0), _c_i32(0)
+        _check(self._lib.pkv_scheduler_request(self._h, int(req_id), ctypes.byref(st), ctypes.byref(nt),
+                                               ctypes.byref(comp), ctypes.byref(pre), None, 0))
+        toks = np.empty(nt.value, dtype=np.int32)
+        _check(self._lib.pkv_scheduler_request(self._h, int(req_id), None, None, None, None,
+                                               _ptr(toks), int(toks.size)))
+        return {"state": st.value, "num_tokens": nt.value, "computed": comp.value,
+                "preemptions": pre.value, "tokens": toks}
 
 
 def blocks_for_bytes(nbytes: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:

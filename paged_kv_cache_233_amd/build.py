@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "allocator.cpp", "sha256.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "allocator.cpp", "scheduler.cpp", "sha256.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
 
 # Packed-FP32 VALU instructions are kept out of all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -336,6 +336,45 @@ int pkv_allocator_enable_prefix_caching(pkv_allocator* a, int32_t enabled) {
   return PKV_OK;
 }
 
+}  // extern "C"
+
+// The cached blocks a prompt would attach (longest run of full blocks from
+// its start whose chained hashes are in the map), and the hash of the last.
+static void walk_cached(const pkv_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                        uint64_t extra_key, int32_t max_cached_tokens, std::vector<int32_t>* got,
+                        Hash* last) {
+  const int32_t limit = max_cached_tokens < 0 ? n_tokens : std::min(n_tokens, max_cached_tokens);
+  const int32_t full = a->caching ? limit / pkv::kBlock : 0;
+  Hash h;
+  for (int32_t k = 0; k < full; ++k) {
+    pkv::block_hash(k > 0 ? last->data() : nullptr, tokens + (int64_t)k * pkv::kBlock,
+                    k == 0 ? extra_key : 0, h.data());
+    auto it = a->cached.find(make_key(h));
+    if (it == a->cached.end()) break;  // chained hashes: every later block misses too
+    got->push_back(it->second);
+    *last = h;
+  }
+}
+
+extern "C" {
+
+int pkv_prefix_lookup(pkv_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                      uint64_t extra_key, int32_t max_cached_tokens, int32_t* out_cached_tokens,
+                      int32_t* out_revived_blocks) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(PKV_ERR_INVALID_ARG, "bad token list");
+  if (!out_cached_tokens || !out_revived_blocks) return fail(PKV_ERR_INVALID_ARG, "NULL output");
+  std::vector<int32_t> got;
+  Hash last;
+  walk_cached(a, tokens, n_tokens, extra_key, max_cached_tokens, &got, &last);
+  int32_t revived = 0;
+  for (int32_t b : got) revived += a->ref[b] == 0;
+  *out_cached_tokens = (int32_t)got.size() * pkv::kBlock;
+  *out_revived_blocks = revived;
+  return PKV_OK;
+}
+
 int pkv_seq_add_cached(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
                        uint64_t extra_key, int32_t max_cached_tokens, int32_t* out_cached_tokens) {
   pkv::clear_error();
@@ -344,19 +383,14 @@ int pkv_seq_add_cached(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, 
   if (a->seqs.count(seq_id)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)seq_id);
   pkv_allocator::Seq s;
   s.salt = extra_key;
-  int32_t limit = max_cached_tokens < 0 ? n_tokens : std::min(n_tokens, max_cached_tokens);
-  int32_t full = a->caching ? limit / pkv::kBlock : 0;
-  Hash h;
-  for (int32_t k = 0; k < full; ++k) {
-    pkv::block_hash(s.has_parent ? s.parent.data() : nullptr, tokens + (int64_t)k * pkv::kBlock,
-                    k == 0 ? extra_key : 0, h.data());
-    auto it = a->cached.find(make_key(h));
-    if (it == a->cached.end()) break;  // chained hashes: every later block misses too
-    int32_t b = it->second;
+  Hash last;
+  walk_cached(a, tokens, n_tokens, extra_key, max_cached_tokens, &s.blocks, &last);
+  for (int32_t b : s.blocks) {
     if (a->ref[b] == 0) a->unlink(b);  // free but cached: revived from the queue
     a->ref[b] += 1;
-    s.blocks.push_back(b);
-    s.parent = h;
+  }
+  if (!s.blocks.empty()) {
+    s.parent = last;
     s.has_parent = true;
   }
   s.len = s.recorded = (int64_t)s.blocks.size() * pkv::kBlock;

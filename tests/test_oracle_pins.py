@@ -161,6 +161,33 @@ def test_prefill_vs_brute():
     check_prefill_vs_brute()
 
 
+def check_attend_sequence():
+    """Dense causal attention of one sequence against the brute-force
+    chunked prefill over the same tokens laid out in a pool, and its closed
+    form at position 0 (the output is v_0)."""
+    rng = np.random.default_rng(21)
+    for hq, hkv, d in ((4, 2, 8), (3, 3, 5)):
+        n = 37
+        k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        kp, vp, table = _single_seq_pools(k, v)
+        pos = [0, 5, 15, 16, 36]
+        q = rng.standard_normal((len(pos), hq, d)).astype(np.float32)
+        out = paged.attend_sequence(q, k, v, pos, 0.6)
+        for i, p in enumerate(pos):
+            ref = np.array(brute.prefill_chunk(q[i:i + 1].astype(np.float64).tolist(), [0, 1], [p + 1],
+                                               kp.astype(np.float64).tolist(),
+                                               vp.astype(np.float64).tolist(), table.tolist(), 0.6))
+            assert np.max(np.abs(out[i] - ref[0])) < 1e-12
+        group = hq // hkv
+        for h in range(hq):
+            assert np.array_equal(out[0, h], v[0, h // group].astype(np.float64))
+
+
+def test_attend_sequence():
+    check_attend_sequence()
+
+
 # --------------------------------------------------------------- closed forms
 def _single_seq_pools(k_tokens, v_tokens):
     """Pools holding one sequence's tokens [n, H, D] in blocks 1, 2, ...
@@ -498,7 +525,7 @@ ALL_CHECKS = [check_block_table_example, check_scatter_roundtrip, check_two_toke
               check_single_token_is_value, check_uniform_scores_give_mean, check_dominant_key,
               check_gqa_mapping, check_placement_and_sharing_invariance, check_causal_mask,
               check_prefill_matches_decode_and_splits, check_allocator_policy,
-              check_allocator_invariants, check_utilisation_formula]
+              check_allocator_invariants, check_utilisation_formula, check_attend_sequence]
 
 
 def _mut_no_scale(q, k, v, scale):
@@ -564,6 +591,13 @@ def _mut_causal_off_by_one(q, cu, lens, kp, vp, table, scale):
 _orig_prefill = paged.prefill_chunk
 
 
+def _mut_sequence_window_short(q, k, v, positions, scale):
+    return _orig_sequence(q, k, v, [max(0, p - 1) for p in positions], scale)
+
+
+_orig_sequence = paged.attend_sequence
+
+
 class _FifoModel(amodel.AllocatorModel):
     def free_seq(self, sid):
         released = []
@@ -607,6 +641,7 @@ MUTANTS = {
     "token offset shifted": (paged, "materialise", _mut_materialise_offset),
     "kv head h % Hkv": (paged, "decode", _mut_gqa_modulo),
     "causal window one short": (paged, "prefill_chunk", _mut_causal_off_by_one),
+    "sequence window one short": (paged, "attend_sequence", _mut_sequence_window_short),
     "FIFO free list": (amodel, "AllocatorModel", _FifoModel),
     "head-first free": (amodel, "AllocatorModel", _HeadFirstModel),
     "no copy-on-write": (amodel, "AllocatorModel", _NoCowModel),

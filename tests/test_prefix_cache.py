@@ -95,8 +95,12 @@ def test_freed_blocks_stay_cached_until_reused(impl):
     free_before = a.num_free()
     a.free_seq(1) if is_m else a.free(1)
     assert a.num_free() == free_before + 4
+    assert a.lookup_cached(prompt) == (3 * B, 3)             # all three would leave the queue
+    assert a.num_free() == free_before + 4                   # the lookup changed nothing
     got = a.add_cached(2, prompt)
     assert got == 3 * B
+    assert a.lookup_cached(prompt) == (3 * B, 0)             # in use now: nothing to revive
+    assert a.lookup_cached(prompt, 0, 2 * B + 15) == (2 * B, 0)
     now = list(a.blocks[2]) if is_m else a.block_table([2], 3)[0][0].tolist()
     assert now == blocks[:3]
     assert a.num_free() == free_before + 1                   # the 3 cached blocks left the queue
@@ -213,6 +217,7 @@ def _fuzz(seed):
             prompt = stem[:cut] + rng.integers(0, 50, int(rng.integers(0, 40))).tolist()
             salt = 0 if rng.random() < 0.85 else 1
             lim = -1 if rng.random() < 0.7 else int(rng.integers(0, len(prompt) + 1))
+            assert c.lookup_cached(prompt, salt, lim) == m.lookup_cached(prompt, salt, lim)
             got_c = c.add_cached(nxt, prompt, salt, lim)
             got_m = m.add_cached(nxt, prompt, salt, lim)
             assert got_c == got_m

@@ -278,3 +278,87 @@ def scaled(name: str, divisor: int, seed_offset: int = 100) -> Workload:
         return custom("mixed/%d" % divisor, seed, dec,
                       chunks=[(c, max(1, 512 // divisor)) for c in cached], **big)
     raise KeyError(name)
+
+
+# ------------------------------------------------------------ request streams
+@dataclasses.dataclass
+class Arrival:
+    step: int              # the step before which the request is queued
+    req_id: int
+    prompt: List[int]      # token ids
+    max_new_tokens: int
+    extra_key: int = 0
+
+
+class RequestStream:
+    """A seeded stream of requests for scheduler-driven runs.
+
+    Token ids come from a small vocabulary; prompts start with a prefix of
+    one of a few shared stems (multiples of 16 tokens, so prefix-cache hits
+    occur) and continue with random ids. A token's K and V depend only on
+    (token id, position), drawn once per pair from tables, so two requests
+    holding the same ids at the same positions hold the same K/V (as a
+    causal model would for a shared prefix). Each request's queries are
+    drawn per (request, position), and the token it "samples" after
+    position p is a seeded draw keyed by (request, p).
+    """
+
+    def __init__(self, seed: int, num_requests: int, *, vocab: int = 32, max_pos: int = 320,
+                 prompt_range: Tuple[int, int] = (1, 160), new_range: Tuple[int, int] = (1, 40),
+                 arrival_span: int = 30, num_q_heads: int = 8, num_kv_heads: int = 2,
+                 head_dim: int = 64, dtype: str = "bf16", salted: float = 0.1):
+        self.seed = seed
+        self.vocab = vocab
+        self.max_pos = max_pos
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.dtype = dtype
+        self.scale = 1.0 / math.sqrt(head_dim)
+        rng = np.random.default_rng(seed)
+        stems = [rng.integers(0, vocab, BLOCK_SIZE * int(rng.integers(1, 6))).tolist()
+                 for _ in range(3)]
+        self.arrivals: List[Arrival] = []
+        for r in range(num_requests):
+            stem = stems[int(rng.integers(0, len(stems)))]
+            keep = BLOCK_SIZE * int(rng.integers(0, len(stem) // BLOCK_SIZE + 1))
+            plen = int(rng.integers(prompt_range[0], prompt_range[1] + 1))
+            prompt = (stem[:keep] + rng.integers(0, vocab, plen).tolist())[:max(plen, 1)]
+            new = int(rng.integers(new_range[0], new_range[1] + 1))
+            new = max(1, min(new, max_pos - len(prompt)))
+            step = int(rng.integers(0, arrival_span + 1))
+            salt = 1 if rng.random() < salted else 0
+            self.arrivals.append(Arrival(step, r, prompt, new, salt))
+        self.arrivals.sort(key=lambda a: (a.step, a.req_id))
+        g = self._gen("kv")
+        shape = (vocab, max_pos, num_kv_heads, head_dim)
+        self._k = torch.randn(shape, generator=g, dtype=torch.float32).to(self.torch_dtype)
+        self._v = torch.randn(shape, generator=g, dtype=torch.float32).to(self.torch_dtype)
+        self._q: Dict[int, torch.Tensor] = {}
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def _gen(self, key: str) -> torch.Generator:
+        h = hashlib.sha256(f"stream:{self.seed}:{key}".encode()).digest()
+        g = torch.Generator()
+        g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
+        return g
+
+    def kv(self, tokens: Sequence[int], positions: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+        """K and V of the given (token id, position) pairs: two [n, Hkv, D]."""
+        t = torch.as_tensor(list(tokens), dtype=torch.long)
+        p = torch.as_tensor(list(positions), dtype=torch.long)
+        return self._k[t, p], self._v[t, p]
+
+    def q(self, req_id: int, positions: Sequence[int]) -> torch.Tensor:
+        """Queries of request req_id at the given positions: [n, Hq, D]."""
+        if req_id not in self._q:
+            g = self._gen(f"q:{req_id}")
+            self._q[req_id] = torch.randn((self.max_pos, self.num_q_heads, self.head_dim),
+                                          generator=g, dtype=torch.float32).to(self.torch_dtype)
+        return self._q[req_id][torch.as_tensor(list(positions), dtype=torch.long)]
+
+    def sampled(self, req_id: int, position: int) -> int:
+        """The token id request req_id "samples" from its output at position."""
+        h = hashlib.sha256(f"stream:{self.seed}:tok:{req_id}:{position}".encode()).digest()
+        return int.from_bytes(h[:4], "little") % self.vocab
