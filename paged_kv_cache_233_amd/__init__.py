@@ -156,6 +156,37 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+class Prepared:
+    """A call whose arguments were checked and marshalled once: calling it
+    makes the same library call again (same buffers, same stream) at the
+    cost of one foreign call. It keeps alive the objects its pointers point
+    into. Kernel entry points return one when given ``prepare=True``; the
+    allocator's ``*_into`` methods too."""
+
+    __slots__ = ("_fn", "_args", "_keep", "_out")
+
+    def __init__(self, fn, args, keep=(), out=None):
+        self._fn = fn
+        self._args = tuple(a if a is None or isinstance(a, ctypes._SimpleCData) or
+                           isinstance(a, ctypes._Pointer) or type(a).__name__ == "CArgObject"
+                           else t(a) for t, a in zip(fn.argtypes, args))
+        self._keep = keep
+        self._out = out
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code:
+            _check(code)
+        return None if self._out is None else self._out.value
+
+
+def _run(fn, args, keep, prepare, out=None):
+    if prepare:
+        return Prepared(fn, args, keep, out)
+    _check(fn(*args))
+    return None if out is None else out.value
+
+
 # --------------------------------------------------------------- allocator
 def sha256(data: bytes) -> bytes:
     """SHA-256 of a byte string (the library's own implementation)."""
@@ -265,14 +296,16 @@ class Allocator:
         return slots, [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(k)]
 
     def batch_append_into(self, sids: np.ndarray, ns: np.ndarray, slots_ptr: int,
-                          pairs: np.ndarray) -> int:
+                          pairs: np.ndarray, prepare: bool = False):
         """Like batch_append, writing slots to raw host memory at slots_ptr
         (e.g. a pinned tensor) and copy pairs to ``pairs`` (int64 [2*k]);
-        returns the number of pairs."""
+        returns the number of pairs. With prepare=True, returns a Prepared
+        call (same arrays each time; it returns the number of pairs)."""
         npairs = _c_i32(0)
-        _check(self._lib.pkv_batch_append(self._h, _ptr(sids), _ptr(ns), int(sids.size), slots_ptr,
-                                          _ptr(pairs), int(pairs.size // 2), ctypes.byref(npairs)))
-        return npairs.value
+        return _run(self._lib.pkv_batch_append,
+                    (self._h, _ptr(sids), _ptr(ns), int(sids.size), slots_ptr, _ptr(pairs),
+                     int(pairs.size // 2), ctypes.byref(npairs)),
+                    (self, sids, ns, pairs), prepare, npairs)
 
     def fork(self, parent: int, child: int) -> None:
         _check(self._lib.pkv_seq_fork(self._h, int(parent), int(child)))
@@ -294,10 +327,12 @@ class Allocator:
         return table, lens
 
     def fill_block_table_into(self, sids: np.ndarray, table_ptr: int, max_blocks: int,
-                              lens_ptr: int) -> None:
-        """Write the table and lengths to raw host memory (e.g. pinned tensors)."""
-        _check(self._lib.pkv_fill_block_table(self._h, _ptr(sids), int(sids.size), table_ptr,
-                                              int(max_blocks), lens_ptr))
+                              lens_ptr: int, prepare: bool = False):
+        """Write the table and lengths to raw host memory (e.g. pinned
+        tensors); prepare=True returns a Prepared call instead."""
+        return _run(self._lib.pkv_fill_block_table,
+                    (self._h, _ptr(sids), int(sids.size), table_ptr, int(max_blocks), lens_ptr),
+                    (self, sids), prepare)
 
     def refcount(self, block: int) -> int:
         out = _c_i32(0)
@@ -448,6 +483,10 @@ def _idx(t, name: str, dtype):
 
 
 def _stream(stream) -> int:
+    """A HIP stream handle from None (torch's current stream), a torch
+    stream, or a raw handle (int)."""
+    if isinstance(stream, int):
+        return stream
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -460,7 +499,7 @@ def _pool_shape(k_cache):
     return int(nb), int(hkv), int(d)
 
 
-def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None, prepare=False):
     """Scatter k_new/v_new [T, Hkv, D] into the pools at slot_mapping (int64 [T])."""
     torch = _torch()
     nb, hkv, d = _pool_shape(k_cache)
@@ -473,13 +512,13 @@ def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None)
     t = int(k_new.shape[0])
     if slot_mapping.numel() != t:
         raise Error(ERR_INVALID_ARG, "slot_mapping must hold %d entries" % t)
-    _check(library().pkv_reshape_and_cache(
+    return _run(library().pkv_reshape_and_cache, (
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
         _dev(v_new, "v_new"), hkv * d, _idx(slot_mapping, "slot_mapping", torch.int64), t, nb, hkv, d,
-        _dtype_code(k_cache), _stream(stream)))
+        _dtype_code(k_cache), _stream(stream)), (k_cache, v_cache, k_new, v_new, slot_mapping), prepare)
 
 
-def stage_copy(dst, src, stream=None) -> None:
+def stage_copy(dst, src, stream=None, prepare=False):
     """Copy src (pinned host or device tensor) into the device tensor dst
     (same number of bytes) with a kernel on the stream."""
     if not dst.is_cuda or not dst.is_contiguous():
@@ -489,7 +528,8 @@ def stage_copy(dst, src, stream=None) -> None:
     nbytes = dst.numel() * dst.element_size()
     if src.numel() * src.element_size() != nbytes:
         raise Error(ERR_INVALID_ARG, "dst and src sizes differ")
-    _check(library().pkv_stage_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)))
+    return _run(library().pkv_stage_copy, (dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)),
+                (dst, src), prepare)
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
@@ -518,7 +558,7 @@ def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_di
 
 
 def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, workspace,
-           stream=None, phase: str = "both") -> None:
+           stream=None, phase: str = "both", prepare=False):
     """Paged decode attention; q/out [S, Hq, D], block_table int32 [S, maxB],
     context_lens int32 [S], workspace a uint8 device tensor of at least
     decode_workspace_size(...) bytes (``decode_workspace`` allocates one).
@@ -536,11 +576,12 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
     fn = {"both": library().pkv_paged_attention_decode,
           "split": library().pkv_paged_attention_decode_split,
           "merge": library().pkv_paged_attention_decode_merge}[phase]
-    _check(fn(
+    return _run(fn, (
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32),
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
+        (out, q, k_cache, v_cache, block_table, context_lens, workspace), prepare)
 
 
 def decode_shared_prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,

@@ -353,3 +353,37 @@ def test_stage_copy_bit_exact():
         assert torch.equal(dst[:nbytes].cpu(), src)
         assert torch.equal(dst2[:nbytes], dsrc)
         assert (dst[nbytes:] == 0xAB).all() and (dst2[nbytes:] == 0xCD).all()
+
+
+def test_prepared_launches_match_plain_calls():
+    """Prepared launches (checked and marshalled once, replayed) give the
+    same bits as the plain calls, for reshape_and_cache and both decode
+    phases."""
+    print("[gpu] prepared launches", flush=True)
+    w = workloads.named("tiny")
+    nat = run_native(w, prefill=False)
+    q = torch.cat([w.seq_q(s) for s in w.decode_seqs]).cuda()
+    table = torch.from_numpy(nat["decode_table"]).cuda()
+    lens = torch.from_numpy(nat["decode_lens"]).cuda()
+    kc, vc = nat["k_cache"].clone(), nat["v_cache"].clone()
+    ws = pkv.decode_workspace(q.shape[0], w.num_q_heads, w.num_kv_heads, w.head_dim)
+    out1 = torch.empty_like(q)
+    split = pkv.decode(out1, q, kc, vc, table, lens, w.scale, ws, phase="split", prepare=True)
+    merge = pkv.decode(out1, q, kc, vc, table, lens, w.scale, ws, phase="merge", prepare=True)
+    for _ in range(3):
+        out1.zero_()
+        split()
+        merge()
+        torch.cuda.synchronize()
+        assert torch.equal(out1, nat["decode"])
+    # reshape: a prepared scatter equals the plain one
+    t = 5
+    kn = torch.randn((t, w.num_kv_heads, w.head_dim)).cuda()
+    vn = torch.randn((t, w.num_kv_heads, w.head_dim)).cuda()
+    slots = torch.tensor([16 * 3 + 1, 16 * 3 + 2, -1, 16 * 7 + 15, 16 * 2], dtype=torch.int64).cuda()
+    k2, v2 = kc.clone(), vc.clone()
+    pkv.reshape_and_cache(kc, vc, kn, vn, slots, prepare=True)()
+    pkv.reshape_and_cache(k2, v2, kn, vn, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int32), k2.view(torch.int32))
+    assert torch.equal(vc.view(torch.int32), v2.view(torch.int32))

@@ -239,3 +239,34 @@ def test_device_entry_points_reject_bad_arguments():
     # copy_blocks: negative count
     assert _raw("pkv_copy_blocks", 16, 16, 16, -1, 4, 1, 128, 1, None) == pkv.ERR_INVALID_ARG
     assert b"head_dim" in pkv.library().pkv_last_error() or True
+
+
+def test_prepared_allocator_calls_match_plain_calls():
+    """A Prepared call repeats the same library call: two allocators driven
+    the same way, one through prepared calls, fill identical buffers."""
+    import paged_kv_cache_233_amd as pkv
+    sids = np.arange(1, 9, dtype=np.int64)
+    ones = np.ones(sids.size, dtype=np.int32)
+    allocs = [pkv.Allocator(64), pkv.Allocator(64)]
+    for a in allocs:
+        for s in sids:
+            a.add(int(s))
+            a.append(int(s), int(3 * s))
+    bufs = [np.zeros(8 + 8 * 12 + 8, dtype=np.int64) for _ in range(2)]
+    pairs = np.empty(16, dtype=np.int64)
+    prep_a = allocs[0].batch_append_into(sids, ones, bufs[0].ctypes.data, pairs, prepare=True)
+    prep_t = allocs[0].fill_block_table_into(sids, bufs[0].ctypes.data + 96, 12,
+                                             bufs[0].ctypes.data + 64, prepare=True)
+    for _ in range(20):
+        assert prep_a() == 0
+        prep_t()
+        assert allocs[1].batch_append_into(sids, ones, bufs[1].ctypes.data, pairs) == 0
+        allocs[1].fill_block_table_into(sids, bufs[1].ctypes.data + 96, 12, bufs[1].ctypes.data + 64)
+        assert np.array_equal(bufs[0], bufs[1])
+    # a failing prepared call raises like the plain one
+    big = np.full(sids.size, 1000, dtype=np.int32)
+    room = np.zeros(int(big.sum()), dtype=np.int64)
+    prep_big = allocs[0].batch_append_into(sids, big, room.ctypes.data, pairs, prepare=True)
+    with pytest.raises(pkv.Error) as e:
+        prep_big()
+    assert e.value.code == pkv.ERR_OUT_OF_BLOCKS
