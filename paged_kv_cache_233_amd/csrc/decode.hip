@@ -297,7 +297,8 @@ decode_split_kernel(DecodeParams p) {
   using Sh = Shape<DT, D>;
   extern __shared__ __align__(16) char lds[];
   int32_t* tiles = reinterpret_cast<int32_t*>(lds);                       // [kTilesPerRound]
-  Piece* pieces = reinterpret_cast<Piece*>(tiles + kTilesPerRound);       // [kPiecesPerRound]
+  int32_t* tile_head = tiles + kTilesPerRound;                            // [kTilesPerRound]
+  Piece* pieces = reinterpret_cast<Piece*>(tile_head + kTilesPerRound);   // [kPiecesPerRound]
   char* qlds = reinterpret_cast<char*>(pieces + kPiecesPerRound);         // [kq][G * kRow]
   const int lane = threadIdx.x;
   const int n = lane & 15;
@@ -405,34 +406,13 @@ decode_split_kernel(DecodeParams p) {
           pc.pad = 0;
           pieces[np] = pc;
         }
-        // Block ids of the piece and the query rows of heads g*G .. g*G+G-1
-        // (contiguous, at most 8 KiB): all loads of a 64-tile chunk are
-        // issued before anything is written, so one memory round trip
-        // stages them.
-        const int32_t* trow = p.block_table + (int64_t)s * p.max_blocks + p.skip + j;
-        const char* qsrc = reinterpret_cast<const char*>(p.q) +
-                           ((int64_t)s * p.num_q_heads + (int64_t)g * G) * Sh::kRow;
-        char* qdst = qlds + np * qbytes;
-        {
-          const int32_t b = lane < cnt ? trow[lane] : 0;
-          uint4 qc[8];
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int32_t o = (lane + 64 * m) * 16;
-            qc[m] = o < qbytes ? *reinterpret_cast<const uint4*>(qsrc + o) : uint4{0u, 0u, 0u, 0u};
-          }
-          if (lane < cnt) tiles[nt + lane] = ((uint32_t)b < (uint32_t)p.num_blocks ? b : 0) * p.num_kv_heads + g;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int32_t o = (lane + 64 * m) * 16;
-            if (o < qbytes) *reinterpret_cast<uint4*>(qdst + o) = qc[m];
-          }
-        }
-        for (int32_t t = 64 + lane; t < cnt; t += 64) {
-          const int32_t b = trow[t];
-          tiles[nt + t] = ((uint32_t)b < (uint32_t)p.num_blocks ? b : 0) * p.num_kv_heads + g;
-        }
-        ++np;
+        // For now each tile holds its index in the block table (and its KV
+        // head); the ids are read below, for all pieces at once.
+        const int32_t tbase = s * p.max_blocks + p.skip + j;
+        for (int32_t t = lane; t < cnt; t += 64) {
+          tiles[nt + t] = tbase + t;
+          tile_head[nt + t] = g;
+        }        ++np;
         nt += cnt;
         i += cnt;
         j += cnt;
@@ -448,6 +428,77 @@ decode_split_kernel(DecodeParams p) {
         if (i < i1) {
           // lengths of the first 64 sequences are still in the scan registers
           len_s = s < 64 ? __builtin_amdgcn_readlane(len0, s) : seq_len_uniform(p, s);
+        }
+      }
+    }
+    __syncthreads();
+    // Block ids of every tile of the round and the query rows of every piece
+    // (heads g*G .. g*G+G-1 of its sequence, contiguous): all loads of a
+    // batch are issued before anything is written, so the round's staging
+    // takes one memory round trip (one per 512 chunks of query rows).
+    {
+      int32_t bid[kTilesPerRound / 64];
+#pragma unroll
+      for (int m = 0; m < kTilesPerRound / 64; ++m) {
+        const int32_t k = lane + 64 * m;
+        bid[m] = k < nt ? p.block_table[tiles[k]] : 0;
+      }
+      const int32_t cpp = qbytes / 16;        // 16-byte chunks per piece
+      const int32_t nq = np * cpp;
+      constexpr int kQ = Sh::kRow > 256 ? 2 : 4;   // query chunks per lane and batch
+      // (a native vector type: the HIP uint4 class copies through memcpy,
+      // which would put these registers in scratch memory)
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      for (int32_t c0 = 0; c0 < nq; c0 += 64 * kQ) {
+        // chunk c = c0 + lane + 64m is 16-byte chunk o of piece q; (q, o)
+        // advance by 64 chunks per m
+        u32x4 qc[kQ];
+        int32_t q = (c0 + lane) / cpp;
+        int32_t o = (c0 + lane) - q * cpp;
+        const int32_t q_first = q, o_first = o;
+#pragma unroll
+        for (int m = 0; m < kQ; ++m) {
+          if (c0 + lane + 64 * m < nq) {
+            const Piece& P = pieces[q];
+            const char* qsrc = reinterpret_cast<const char*>(p.q) +
+                               ((int64_t)P.s * p.num_q_heads + (int64_t)P.g * G) * Sh::kRow;
+            qc[m] = *reinterpret_cast<const u32x4*>(qsrc + 16 * o);
+          }
+          o += 64;
+          while (o >= cpp) {
+            o -= cpp;
+            ++q;
+          }
+        }
+        if (c0 == 0) {
+#pragma unroll
+          for (int m = 0; m < kTilesPerRound / 64; ++m) {
+            const int32_t k = lane + 64 * m;
+            if (k < nt)
+              tiles[k] = ((uint32_t)bid[m] < (uint32_t)p.num_blocks ? bid[m] : 0) * p.num_kv_heads +
+                         tile_head[k];
+          }
+        }
+        q = q_first;
+        o = o_first;
+#pragma unroll
+        for (int m = 0; m < kQ; ++m) {
+          if (c0 + lane + 64 * m < nq)
+            *reinterpret_cast<u32x4*>(qlds + q * qbytes + 16 * o) = qc[m];
+          o += 64;
+          while (o >= cpp) {
+            o -= cpp;
+            ++q;
+          }
+        }
+      }
+      if (nq == 0) {
+#pragma unroll
+        for (int m = 0; m < kTilesPerRound / 64; ++m) {
+          const int32_t k = lane + 64 * m;
+          if (k < nt)
+            tiles[k] = ((uint32_t)bid[m] < (uint32_t)p.num_blocks ? bid[m] : 0) * p.num_kv_heads +
+                       tile_head[k];
         }
       }
     }
@@ -559,7 +610,7 @@ int decode_depth() {
 // Dynamic LDS of the split kernel: tile list, pieces, query rows.
 template <int DT, int D>
 size_t split_lds_bytes(const DecodeParams& prm) {
-  return (size_t)kTilesPerRound * 4 + kPiecesPerRound * sizeof(Piece) +
+  return (size_t)kTilesPerRound * 8 + kPiecesPerRound * sizeof(Piece) +
          (size_t)prm.pieces_per_round * prm.group * Shape<DT, D>::kRow;
 }
 
