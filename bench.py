@@ -594,7 +594,8 @@ def cpu_baseline(w, nseq):
             paged.decode(q, ora["k_cache"], ora["v_cache"], table, lens, w.scale)
             reps += 1
             el = time.perf_counter() - t0
-            if el > 10.0 or reps >= 20:
+            # about 10 s of CPU work (bounded in case the host is very slow)
+            if el > 10.0 or reps >= 200:
                 break
     tokens = int(lens.sum())
     kv = float(tokens) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
