@@ -156,6 +156,10 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+# ctypes objects passed through as they are (values, pointers, byref())
+_CTYPES_ARGS = (ctypes._SimpleCData, ctypes._Pointer, type(ctypes.byref(ctypes.c_int32())))
+
+
 class Prepared:
     """A call whose arguments were checked and marshalled once: calling it
     makes the same library call again (same buffers, same stream) at the
@@ -167,9 +171,10 @@ class Prepared:
 
     def __init__(self, fn, args, keep=(), out=None):
         self._fn = fn
-        self._args = tuple(a if a is None or isinstance(a, ctypes._SimpleCData) or
-                           isinstance(a, ctypes._Pointer) or type(a).__name__ == "CArgObject"
-                           else t(a) for t, a in zip(fn.argtypes, args))
+        # plain Python values are converted to their ctypes argument types
+        # now, so that a call converts nothing
+        self._args = tuple(a if a is None or isinstance(a, _CTYPES_ARGS) else t(a)
+                           for t, a in zip(fn.argtypes, args))
         self._keep = keep
         self._out = out
 
