@@ -114,15 +114,30 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, const State
   }
 }
 
-// Logical wave whose tile range holds flat tile i: the largest w with
-// floor(w*total/W) <= i.
-__device__ __forceinline__ int32_t wave_of(int64_t i, int64_t total, int32_t W) {
-  return (int32_t)(((i + 1) * W + total - 1) / total - 1);
-}
-
-__device__ __forceinline__ bool wave_empty(int32_t w, int64_t total, int32_t W) {
-  return total * w / W == total * (w + 1) / W;
-}
+// The waves' flat tile ranges: wave w takes [begin(w), begin(w + 1)) with
+// begin(w) = floor(total * w / W). total < 2^31 (the host bounds sequences x
+// heads x table width) and W < 2^15, so with total = q W + r,
+// begin(w) = q w + (r w) / W stays in 32-bit arithmetic (64-bit divisions
+// are long software sequences on the GPU).
+struct WaveRanges {
+  int32_t q, r, W;
+  float w_per_tile;
+  __device__ __forceinline__ WaveRanges(int32_t total, int32_t W_) : W(W_) {
+    q = total / W;
+    r = total - q * W;
+    w_per_tile = (float)W / (float)max(total, 1);
+  }
+  __device__ __forceinline__ int32_t begin(int32_t w) const { return q * w + (r * w) / W; }
+  __device__ __forceinline__ bool empty(int32_t w) const { return begin(w) == begin(w + 1); }
+  // The wave whose range holds tile i: the largest w with begin(w) <= i
+  // (an estimate in float, then exact steps).
+  __device__ __forceinline__ int32_t owner(int32_t i) const {
+    int32_t w = min(max((int32_t)(((float)i + 0.5f) * w_per_tile), 0), W - 1);
+    while (w > 0 && begin(w) > i) --w;
+    while (w + 1 < W && begin(w + 1) <= i) ++w;
+    return w;
+  }
+};
 
 // Softmax state of query row `row` folded from the prefix states: lane
 // (n, kg) of the tile layout gets dims (4kg + i) * (D/16) + e.
@@ -201,13 +216,12 @@ __device__ __forceinline__ void zero_rows(const DecodeParams& p, int32_t s) {
 // the sequence holds its state in its second slot, every other wave in its
 // first.
 template <int DT, int D>
-__device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int64_t first,
-                               int64_t last, int64_t total) {
+__device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t first,
+                               int32_t last, const WaveRanges& R) {
   const int lane = threadIdx.x;
   const int32_t G = p.group;
-  const int32_t W = p.num_waves;
   const int64_t out_row = ((int64_t)s * p.num_q_heads + (int64_t)g * G) * D;
-  const int32_t w0 = wave_of(first, total, W), w1 = wave_of(last, total, W);
+  const int32_t w0 = R.owner(first), w1 = R.owner(last);
   const int32_t stride = G * (D + 4);
   for (int32_t e = 8 * lane; e < G * D; e += 512) {
     const int32_t h = e / D;
@@ -218,8 +232,8 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int6
       int32_t slot[4];
       int cnt = 0;
       for (; wv <= w1 && cnt < 4; ++wv) {
-        if (wave_empty(wv, total, W)) continue;
-        slot[cnt++] = 2 * wv + (total * wv / W < first ? 1 : 0);
+        if (R.empty(wv)) continue;
+        slot[cnt++] = 2 * wv + (R.begin(wv) < first ? 1 : 0);
       }
       float4 o0[4], o1[4];
       float mk[4], lk[4];
@@ -340,14 +354,14 @@ decode_split_kernel(DecodeParams p) {
     }
     per_head += __builtin_amdgcn_readlane(incl, 63);
   }
-  const int64_t total = (int64_t)per_head * p.num_kv_heads;
-  const int64_t i0 = total * w / p.num_waves;
-  const int64_t i1 = total * (w + 1) / p.num_waves;
+  const WaveRanges R(per_head * p.num_kv_heads, p.num_waves);
+  const int32_t i0 = R.begin(w);
+  const int32_t i1 = R.begin(w + 1);
   if (i0 >= i1) return;
 
   // Locate the (head, sequence) holding tile i0.
-  int32_t g = (int32_t)(i0 / per_head);
-  const int32_t r = (int32_t)(i0 - (int64_t)g * per_head);
+  int32_t g = i0 / per_head;
+  const int32_t r = i0 - g * per_head;
   int32_t s = 0, seq_start = 0, len_s = 0;
   {
     int32_t start = 0;
@@ -583,11 +597,11 @@ decode_merge_kernel(DecodeParams p) {
   const int32_t a = p.ws_prefix[s];
   const int32_t b = p.ws_prefix[s + 1];
   if (a == b) return;
-  const int64_t total = (int64_t)per_head * p.num_kv_heads;
-  const int64_t first = (int64_t)g * per_head + a;
-  const int64_t last = (int64_t)g * per_head + b - 1;
-  if (wave_of(first, total, p.num_waves) == wave_of(last, total, p.num_waves)) return;
-  merge_sequence<DT, D>(p, s, g, first, last, total);
+  const WaveRanges R(per_head * p.num_kv_heads, p.num_waves);
+  const int32_t first = g * per_head + a;
+  const int32_t last = g * per_head + b - 1;
+  if (R.owner(first) == R.owner(last)) return;
+  merge_sequence<DT, D>(p, s, g, first, last, R);
 }
 
 int g_waves_device = -1;
