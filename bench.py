@@ -60,6 +60,8 @@ def parse():
                     help="per-step indices to the device: copied by a kernel (pkv_stage_copy), "
                          "copied by the DMA engine (hipMemcpyAsync), or read in place from "
                          "pinned host memory")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the plain streaming copy/sum measurement reported beside the roofline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--shared-probe", action="store_true",
@@ -80,6 +82,53 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def stream_leg(dev):
+    """What plain streaming reaches on this GPU, as the practical ceiling
+    beside the decode roofline: the library's streaming-read kernel over
+    2 GiB (best of three grid sizes), and a torch device-to-device copy of
+    2 GiB (read + written bytes) for comparison; each the median of 10 timed
+    runs over four buffers in turn (8 GiB, past the last-level cache)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+
+    n = 2 << 30
+    bufs = [torch.ones(n // 2, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    dst = torch.empty_like(bufs[0])
+    words = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        out = []
+        for r in range(13):
+            e0, e1 = hip.create(), hip.create()
+            hip.record(e0, sh)
+            fn(bufs[r % 4])
+            hip.record(e1, sh)
+            torch.cuda.synchronize()
+            if r >= 3:
+                out.append(hip.elapsed_us(e0, e1))
+        return float(np.median(out))
+
+    read = {}
+    for wg in (1024, 2048, 4096):
+        read[wg] = n / timed(lambda b: pkv.stream_read(b, words, wg, stream=sh)) / 1e3
+    best = max(read, key=read.get)
+    copy_us = timed(lambda b: dst.copy_(b))
+    del bufs, dst
+    torch.cuda.empty_cache()
+    r = {"read_gbs": round(read[best], 1), "read_workgroups": best,
+         "torch_copy_gbs": round(2 * n / copy_us / 1e3, 1),
+         "what": "pkv_stream_read over 2 GiB (read bytes; best of 1024/2048/4096 workgroups) and "
+                 "a torch device-to-device copy of 2 GiB (read + written bytes); median of 10, "
+                 "four buffers in turn"}
+    log("streaming: read %.1f GB/s (%d workgroups), torch copy %.1f GB/s"
+        % (r["read_gbs"], best, r["torch_copy_gbs"]))
+    return r
 
 
 class HipEvents:
@@ -350,6 +399,7 @@ def main():
 
     prefill = None if args.no_prefill else prefill_leg(args, dev)
     shared = None if args.no_shared else shared_leg(args, dev)
+    stream = None if args.no_stream else stream_leg(dev)
 
     # ------------------------------------------------------- CPU oracle leg
     cpu = None
@@ -394,6 +444,8 @@ def main():
         "graph_step": graph,
         "prefill": prefill,
         "shared_prefix": shared,
+        "streaming": None if stream is None else dict(
+            stream, split_kernel_pct_of_read=round(100 * achieved / stream["read_gbs"], 1)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -308,6 +308,14 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t 
  * overlapping; `bytes` may be any size. The host must leave src unchanged
  * until the copy has run. */
 int pkv_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
+/* Measurement aid, not part of the attention path: a plain streaming read of
+ * `bytes` of device memory at src (both multiples of 16) by `workgroups`
+ * workgroups of 256 threads, each reading one contiguous slice with 16-byte
+ * loads; workgroup b writes one word folded from its data to out[b] (device
+ * memory, `workgroups` words), so the reads cannot be dropped. Timing it
+ * gives the read bandwidth plain streaming reaches on the device, the
+ * practical ceiling of the HBM-bound decode. */
+int pkv_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgroups, void* stream);
 
 /* Workspace bytes pkv_paged_attention_decode needs for these sizes on the
  * current device (split-KV partial results and bookkeeping). The size does

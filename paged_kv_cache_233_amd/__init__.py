@@ -62,6 +62,7 @@ _SIGNATURES = {
     "pkv_seq_len": ([_c_p, _c_i64, _c_p], ctypes.c_int),
     "pkv_allocator_enable_prefix_caching": ([_c_p, _c_i32], ctypes.c_int),
     "pkv_seq_add_cached": ([_c_p, _c_i64, _c_p, _c_i32, ctypes.c_uint64, _c_i32, _c_p], ctypes.c_int),
+    "pkv_stream_read": ([_c_p, _c_sz, _c_p, _c_i32, _c_p], ctypes.c_int),
     "pkv_prefix_lookup": ([_c_p, _c_p, _c_i32, ctypes.c_uint64, _c_i32, _c_p, _c_p], ctypes.c_int),
     "pkv_scheduler_create": ([_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p], ctypes.c_int),
     "pkv_scheduler_destroy": ([_c_p], ctypes.c_int),
@@ -535,6 +536,20 @@ def stage_copy(dst, src, stream=None, prepare=False):
         raise Error(ERR_INVALID_ARG, "dst and src sizes differ")
     return _run(library().pkv_stage_copy, (dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)),
                 (dst, src), prepare)
+
+
+def stream_read(src, out, workgroups: int, stream=None, prepare=False):
+    """Plain streaming read of the device tensor src (a measurement aid):
+    `workgroups` workgroups each read one contiguous slice and write one
+    folded word to out (uint32 device tensor of at least `workgroups`
+    words)."""
+    if not src.is_cuda or not src.is_contiguous() or not out.is_cuda:
+        raise Error(ERR_INVALID_ARG, "src and out must be contiguous device tensors")
+    if out.numel() * out.element_size() < 4 * int(workgroups):
+        raise Error(ERR_INVALID_ARG, "out holds fewer than %d words" % int(workgroups))
+    nbytes = src.numel() * src.element_size()
+    return _run(library().pkv_stream_read, (src.data_ptr(), nbytes, out.data_ptr(), int(workgroups),
+                                            _stream(stream)), (src, out), prepare)
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:

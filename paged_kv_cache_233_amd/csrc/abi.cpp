@@ -122,6 +122,18 @@ int pkv_stage_copy(void* dst, const void* src, size_t bytes, void* stream) {
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "stage_copy launch");
 }
 
+int pkv_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgroups, void* stream) {
+  pkv::clear_error();
+  if (bytes == 0) return PKV_OK;
+  if (!src || !out) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((uintptr_t)src % 16 != 0 || bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "src and bytes must be multiples of 16");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(PKV_ERR_INVALID_ARG, "workgroups %d outside [1, 2^20]", workgroups);
+  hipError_t err = pkv::launch_stream_read(src, bytes, out, workgroups, (hipStream_t)stream);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "stream_read launch");
+}
+
 int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, size_t* out) {
   pkv::clear_error();

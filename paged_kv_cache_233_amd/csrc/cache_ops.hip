@@ -74,9 +74,39 @@ stage_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, int64_
   if (blockIdx.x == 0 && (int32_t)threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
+// Streaming read: workgroup b reads the b-th of gridDim.x equal contiguous
+// slices with 16-byte loads, four in flight per thread, and writes one word
+// folded from what it read (so that the loads stay live).
+__global__ void __launch_bounds__(256)
+stream_read_kernel(const uint4* __restrict__ src, int64_t vecs, uint32_t* __restrict__ out) {
+  const int64_t per = (vecs + gridDim.x - 1) / gridDim.x;
+  const int64_t b = per * blockIdx.x;
+  const int64_t e = min(b + per, vecs);
+  uint32_t acc = 0;
+  for (int64_t i = b + threadIdx.x; i < e; i += 4 * 256) {
+    uint4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = i + u * 256;
+      x[u] = j < e ? src[j] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+  }
+  // one word per workgroup: lane 0 of wave 0 keeps its own fold
+  if (threadIdx.x == 0) out[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 namespace pkv {
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgroups,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                     (const uint4*)src, (int64_t)(bytes / 16), out);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   const int64_t vecs = (int64_t)(bytes / 16);

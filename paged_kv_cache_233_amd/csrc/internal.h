@@ -36,6 +36,10 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
                                     hipStream_t stream);
 
 hipError_t launch_stage_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+// Plain streaming read of `bytes` (a multiple of 16) by `workgroups`
+// workgroups; one folded word per workgroup to out[workgroups].
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgroups,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t n,
                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                               int32_t dtype, hipStream_t stream);

@@ -387,3 +387,26 @@ def test_prepared_launches_match_plain_calls():
     torch.cuda.synchronize()
     assert torch.equal(kc.view(torch.int32), k2.view(torch.int32))
     assert torch.equal(vc.view(torch.int32), v2.view(torch.int32))
+
+
+def test_stream_read_folds_what_it_reads():
+    """The streaming-read measurement kernel: workgroup b's word is the XOR
+    fold of the 16-byte vectors its first thread read (every 256th vector of
+    the b-th slice)."""
+    print("[gpu] stream_read", flush=True)
+    rng = np.random.default_rng(5)
+    vecs = 256 * 37 + 19
+    host = rng.integers(0, 2**32, size=(vecs, 4), dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32).copy()).cuda()
+    wg = 7
+    out = torch.zeros(wg, dtype=torch.int32, device="cuda")
+    pkv.stream_read(src, out, wg)
+    torch.cuda.synchronize()
+    per = -(-vecs // wg)
+    got = out.cpu().numpy().view(np.uint32)
+    for b in range(wg):
+        lo, hi = b * per, min(b * per + per, vecs)
+        acc = np.uint32(0)
+        for j in range(lo, hi, 256):
+            acc ^= np.bitwise_xor.reduce(host[j])
+        assert got[b] == acc, b
