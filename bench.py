@@ -428,6 +428,8 @@ def main():
                    "index_staging": args.stage, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
+        # one layer's kernels only: reshape_and_cache + split + merge
+        "kernel_tokens_per_s": round(S / ((rc_us.mean() + dec_us.mean()) * 1e-6), 1),
         "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
                       "decode_median": round(float(np.median(dec_us)), 2),
                       "decode_split_kernel_mean": round(float(split_us.mean()), 2),
