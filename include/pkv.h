@@ -234,7 +234,9 @@ int pkv_scheduler_create(pkv_allocator* alloc, int32_t token_budget, int32_t lon
                          int32_t chunked_prefill, int32_t max_num_seqs, pkv_scheduler** out);
 int pkv_scheduler_destroy(pkv_scheduler* s);
 /* Queue a request (prompt_len >= 1 token ids, copied). PKV_ERR_SEQ_EXISTS
- * if the id was used before. */
+ * if the id was used before; PKV_ERR_OUT_OF_BLOCKS (nothing queued) if its
+ * prompt_len + max_new_tokens - 1 tokens need more blocks than the pool
+ * holds, so that it could never finish. */
 int pkv_scheduler_add_request(pkv_scheduler* s, int64_t req_id, const int32_t* prompt,
                               int32_t prompt_len, int32_t max_new_tokens, uint64_t extra_key);
 /* Plan one step: sizes of the plan (outputs may be NULL). The allocator

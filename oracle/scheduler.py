@@ -40,6 +40,8 @@ Readings where the pages are silent:
 * At admission, with prefix caching on, the request's tokens are looked up
   and the cached full blocks attached (at most all tokens but one, so a
   step always has a position to sample from); they count as computed.
+* A request whose tokens (all but the last sampled one) need more blocks
+  than the pool holds is refused when it is queued: it could never finish.
 * A request is admitted only if its lookup hits plus new blocks fit the
   free queue (checked before anything changes), so a failed admission
   leaves the allocator untouched; the waiting walk stops there.
@@ -116,6 +118,9 @@ class SchedulerModel:
             raise KeyError("request exists")
         if len(prompt) < 1 or max_new_tokens < 1:
             raise ValueError("empty prompt or nothing to generate")
+        need = -(-(len(prompt) + max_new_tokens - 1) // BLOCK)
+        if need > self.alloc.num_blocks - 1:
+            raise OutOfBlocks("request needs more blocks than the pool holds")
         self.requests[req_id] = Request(req_id, [int(t) for t in prompt], int(max_new_tokens),
                                         int(extra_key))
         self.waiting.append(req_id)

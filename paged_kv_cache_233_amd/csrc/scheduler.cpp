@@ -55,6 +55,7 @@ struct Item {
 
 struct pkv_scheduler {
   pkv_allocator* alloc = nullptr;
+  int32_t capacity = 0;           // blocks a sequence can ever hold (the pool less the null block)
   int32_t budget = 0;
   int32_t threshold = 0;
   bool chunked = true;
@@ -185,8 +186,11 @@ int pkv_scheduler_create(pkv_allocator* alloc, int32_t token_budget, int32_t lon
   if (!alloc || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
   if (token_budget < 1 || long_prefill_threshold < 0 || max_num_seqs < 0)
     return fail(PKV_ERR_INVALID_ARG, "token_budget must be >= 1, threshold and max_num_seqs >= 0");
+  pkv_stats st;
+  if (int e = pkv_allocator_stats(alloc, &st)) return e;
   pkv_scheduler* s = new pkv_scheduler();
   s->alloc = alloc;
+  s->capacity = st.used_blocks + st.free_blocks;
   s->budget = token_budget;
   s->threshold = long_prefill_threshold;
   s->chunked = chunked_prefill != 0;
@@ -210,6 +214,13 @@ int pkv_scheduler_add_request(pkv_scheduler* s, int64_t req_id, const int32_t* p
   if ((int64_t)prompt_len + max_new_tokens > INT32_MAX / 2)
     return fail(PKV_ERR_INVALID_ARG, "request too long");
   if (s->reqs.count(req_id)) return fail(PKV_ERR_SEQ_EXISTS, "request %lld exists", (long long)req_id);
+  // At its end a request holds the K/V of all its tokens but the last
+  // sampled one; one that needs more blocks than the pool has could never
+  // finish (and would hold up the queue behind it).
+  const int32_t need = (prompt_len + max_new_tokens - 1 + pkv::kBlock - 1) / pkv::kBlock;
+  if (need > s->capacity)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "request %lld needs %d blocks, the pool holds %d",
+                (long long)req_id, need, s->capacity);
   Request r;
   r.tokens.assign(prompt, prompt + prompt_len);
   r.prompt_len = prompt_len;

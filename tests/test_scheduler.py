@@ -181,15 +181,16 @@ def test_preempted_request_readmitted_first(impl):
 
 @pytest.mark.parametrize("impl", IMPLS)
 def test_request_preempts_itself(impl):
-    """A request that is the last running one and cannot grow is preempted
-    itself and the running walk stops there."""
-    s = Both(impl, 3, 64)                          # 2 usable blocks
-    s.add(1, list(range(32)), 5)
+    """When the request being placed is itself the last admitted one, it is
+    the one preempted, and the running walk stops there."""
+    s = Both(impl, 5, 64)                          # 4 usable blocks
+    s.add(1, list(range(20)), 10)                  # 2 blocks; position 20 still fits its last block
+    s.add(2, list(range(100, 132)), 10)            # 2 blocks; position 32 needs a third
     rows, pre, _, _ = s.step()
-    assert rows == [(1, 0, 32, True)]
+    assert rows == [(1, 0, 20, True), (2, 0, 32, True)]
     rows, pre, _, _ = s.step()
-    assert pre == [1] and rows == []
-    assert s.counts() == (1, 0)
+    assert rows == [(1, 20, 1, True)] and pre == [2]
+    assert s.counts() == (1, 1)
 
 
 @pytest.mark.parametrize("impl", IMPLS)
@@ -224,6 +225,18 @@ def test_max_num_seqs_bounds_running(impl):
     rows, _, _, _ = s.step()
     assert [x[0] for x in rows] == [0, 1]
     assert s.counts() == (2, 2)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_request_longer_than_the_pool_is_refused(impl):
+    """A request whose tokens need more blocks than the whole pool could
+    never finish; it is refused when queued and nothing is queued."""
+    s = Both(impl, 5, 64)                          # 4 usable blocks: 64 tokens
+    err = pkv.Error if impl == "cpp" else amodel.OutOfBlocks
+    with pytest.raises(err):
+        s.add(1, list(range(60)), 6)               # 65 tokens held at the end
+    s.add(2, list(range(60)), 5)                   # exactly 64: fits
+    assert s.counts() == (1, 0)
 
 
 def test_errors():
