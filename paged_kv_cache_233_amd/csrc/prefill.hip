@@ -609,10 +609,6 @@ prefill_lds_kernel(LdsParams lp) {
     // softmax and PV product, store tile i+1 into the other buffer, which
     // tile i-1 used. Near the round's end a step fetches the last tile again
     // and stores it into the buffer no later step reads.
-    // Step i: fetch tile i+1 from global memory, score tile i and take its
-    // softmax and PV product, store tile i+1 into the other buffer, which
-    // tile i-1 used. Near the round's end a step fetches the last tile again
-    // and stores it into the buffer no later step reads.
     Staged<D> st;
     tile_fetch<D>(st, ln, kbase, vbase, block_stride, s_ids, 0);
     tile_store<D>(st, ln, bufs, pos(0), lim_wg);
