@@ -260,6 +260,12 @@ int pkv_scheduler_plan(pkv_scheduler* s, int64_t* req_ids, int32_t* start_pos, i
 int pkv_scheduler_update(pkv_scheduler* s, const int32_t* sampled, int32_t n_sampled,
                          int32_t* out_num_finished);
 int pkv_scheduler_finished(pkv_scheduler* s, int64_t* req_ids);
+/* Drop a request in any state: a waiting one leaves the queue, a running one
+ * has its blocks freed (an abort), a finished one has its record (and token
+ * ids) released; its id may then be used again. Refused while a plan is
+ * pending. Finished requests are kept until removed, so that their tokens
+ * can be read. */
+int pkv_scheduler_remove_request(pkv_scheduler* s, int64_t req_id);
 int pkv_scheduler_counts(pkv_scheduler* s, int32_t* num_waiting, int32_t* num_running);
 /* One request: state (0 waiting, 1 running, 2 finished), tokens held,
  * computed count, times preempted, and (if tokens != NULL, max_tokens >=

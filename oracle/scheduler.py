@@ -195,6 +195,22 @@ class SchedulerModel:
         self.last_plan = Plan(out, pairs, preempted)
         return self.last_plan
 
+    def remove_request(self, req_id: int) -> None:
+        """Drop a request in any state (dequeue, abort with its blocks freed,
+        or release a finished one)."""
+        if self.last_plan is not None:
+            raise RuntimeError("a plan is pending")
+        if req_id not in self.requests:
+            raise KeyError("no such request")
+        if req_id in self.running:
+            self.alloc.free_seq(req_id)
+            self.running.remove(req_id)
+        elif req_id in self.waiting:
+            self.waiting.remove(req_id)
+        elif req_id in self.finished:
+            self.finished.remove(req_id)
+        del self.requests[req_id]
+
     def update(self, sampled: Sequence[int]) -> List[int]:
         """The step ran: record the computed tokens' ids, advance the counts,
         append one sampled token (in plan order) to each request the plan

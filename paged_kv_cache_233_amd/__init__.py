@@ -71,6 +71,7 @@ _SIGNATURES = {
     "pkv_scheduler_plan": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "pkv_scheduler_update": ([_c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
     "pkv_scheduler_finished": ([_c_p, _c_p], ctypes.c_int),
+    "pkv_scheduler_remove_request": ([_c_p, _c_i64], ctypes.c_int),
     "pkv_scheduler_counts": ([_c_p, _c_p, _c_p], ctypes.c_int),
     "pkv_scheduler_request": ([_c_p, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32], ctypes.c_int),
     "pkv_seq_record_tokens": ([_c_p, _c_i64, _c_p, _c_i32], ctypes.c_int),
@@ -426,6 +427,11 @@ class Scheduler:
         out = np.empty(nf.value, dtype=np.int64)
         _check(self._lib.pkv_scheduler_finished(self._h, _ptr(out)))
         return out
+
+    def remove_request(self, req_id: int) -> None:
+        """Drop a request: dequeue it, abort it (blocks freed) or release a
+        finished one's record."""
+        _check(self._lib.pkv_scheduler_remove_request(self._h, int(req_id)))
 
     def counts(self) -> Tuple[int, int]:
         w, r = _c_i32(0), _c_i32(0)

@@ -296,6 +296,22 @@ int pkv_scheduler_update(pkv_scheduler* s, const int32_t* sampled, int32_t n_sam
   return PKV_OK;
 }
 
+int pkv_scheduler_remove_request(pkv_scheduler* s, int64_t req_id) {
+  pkv::clear_error();
+  if (int e = check(s)) return e;
+  if (s->pending) return fail(PKV_ERR_INVALID_ARG, "a plan is pending: update it first");
+  auto it = s->reqs.find(req_id);
+  if (it == s->reqs.end()) return fail(PKV_ERR_NO_SUCH_SEQ, "no request %lld", (long long)req_id);
+  if (it->second.state == kRunning) {
+    if (int e = pkv_seq_free(s->alloc, req_id)) return e;
+    s->running.erase(std::find(s->running.begin(), s->running.end(), req_id));
+  } else if (it->second.state == kWaiting) {
+    s->waiting.erase(std::find(s->waiting.begin(), s->waiting.end(), req_id));
+  }
+  s->reqs.erase(it);
+  return PKV_OK;
+}
+
 int pkv_scheduler_finished(pkv_scheduler* s, int64_t* req_ids) {
   pkv::clear_error();
   if (int e = check(s)) return e;

@@ -239,6 +239,39 @@ def test_request_longer_than_the_pool_is_refused(impl):
     assert s.counts() == (1, 0)
 
 
+@pytest.mark.parametrize("impl", IMPLS)
+def test_remove_request_in_each_state(impl):
+    """A waiting request leaves the queue, a running one is aborted with its
+    blocks freed, a finished one's record is released; the id can be used
+    again. Removal is refused while a plan is pending."""
+    s = Both(impl, 16, 128)
+    free0 = s.alloc.num_free()
+    s.add(1, list(range(20)), 1)                   # finishes in its first step
+    s.add(2, list(range(40)), 10)
+    s.add(3, list(range(30)), 10)
+    if impl == "cpp":
+        s.s.schedule()
+        with pytest.raises(pkv.Error):
+            s.s.remove_request(3)
+        s.s.update([7, 7, 7])
+    else:
+        s.s.schedule()
+        with pytest.raises(RuntimeError):
+            s.s.remove_request(3)
+        s.s.update([7, 7, 7])
+    # 1 finished, 2 and 3 running
+    s.s.remove_request(2)                          # abort: its 3 blocks go back
+    s.s.remove_request(1)                          # release the finished record
+    assert s.counts() == (0, 1)
+    assert s.alloc.num_free() == free0 - 2         # only request 3's two blocks are held
+    s.add(4, [1, 2, 3], 2)
+    s.s.remove_request(4)                          # still waiting: dequeued
+    assert s.counts() == (0, 1)
+    s.add(2, [9] * 5, 1)                           # the aborted id is free again
+    rows, _, fin, _ = s.step()
+    assert rows == [(3, 30, 1, True), (2, 0, 5, True)] and fin == [2]
+
+
 def test_errors():
     a = pkv.Allocator(8)
     with pytest.raises(pkv.Error):
@@ -281,6 +314,7 @@ def _fuzz(seed):
     # a request must fit the pool on its own, or it would wait forever
     cap = (nb - 1) * B
     nxt, stats = 0, {"preempted": 0, "chunks": 0, "finished": 0}
+    removed = set()
     for step in range(300):
         if rng.random() < 0.35:
             for _ in range(int(rng.integers(1, 4))):
@@ -294,6 +328,20 @@ def _fuzz(seed):
                 c.add(nxt, prompt, max_new, salt)
                 m.add(nxt, prompt, max_new, salt)
                 nxt += 1
+        if nxt > 0 and rng.random() < 0.08:
+            # drop a request, whatever its state (unknown ids are refused alike)
+            rid = int(rng.integers(0, nxt))
+            try:
+                m.s.remove_request(rid)
+                gone = True
+            except KeyError:
+                gone = False
+            if gone:
+                c.s.remove_request(rid)
+                removed.add(rid)
+            else:
+                with pytest.raises(pkv.Error):
+                    c.s.remove_request(rid)
         tok = int(rng.integers(0, 30))
         r1 = c.step(lambda rid: (tok + rid) % 30)
         r2 = m.step(lambda rid: (tok + rid) % 30)
@@ -308,7 +356,8 @@ def _fuzz(seed):
         if caching:
             assert c.alloc.prefix_cache_stats() == m.alloc.cache_stats()
     for rid in range(nxt):
-        assert c.req(rid) == m.req(rid)
+        if rid not in removed:
+            assert c.req(rid) == m.req(rid)
     return stats
 
 
