@@ -84,6 +84,59 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+def scheduler_leg():
+    """Host cost of the step scheduler (C++): a seeded stream of 256 requests
+    (prompts U[64, 1024], 32..128 generated tokens each, all queued at once)
+    run to completion over a pool of 40% of the blocks they would hold
+    together (so preemption happens), token budget 2048, prefix caching on,
+    no kernels (the sampled tokens are a fixed function of request and
+    position). Reports microseconds per step for schedule + plan copy-out +
+    update through the Python binding."""
+    import numpy as np
+
+    import paged_kv_cache_233_amd as pkv
+
+    rng = np.random.default_rng(11)
+    stems = [rng.integers(0, 32000, 16 * int(rng.integers(2, 20))).astype(np.int32) for _ in range(8)]
+    reqs = []
+    for r in range(256):
+        stem = stems[int(rng.integers(0, len(stems)))]
+        plen = int(rng.integers(64, 1025))
+        keep = 16 * int(rng.integers(0, len(stem) // 16 + 1))
+        prompt = np.concatenate([stem[:keep], rng.integers(0, 32000, plen).astype(np.int32)])[:plen]
+        reqs.append((r, prompt, int(rng.integers(32, 129))))
+    need = sum(-(-(len(p) + n - 1) // 16) for _, p, n in reqs)
+    alloc = pkv.Allocator(int(0.4 * need) + 1)
+    alloc.enable_prefix_caching()
+    sched = pkv.Scheduler(alloc, 2048)
+    for r, p, n in reqs:
+        sched.add_request(r, p, n)
+    steps = tokens = preempted = 0
+    t0 = time.perf_counter()
+    while True:
+        plan = sched.schedule()
+        if len(plan.req_ids) == 0:
+            sched.update([])
+            if sched.counts() == (0, 0):
+                break
+            continue
+        sampled = ((plan.req_ids[plan.samples] * 7 + (plan.start + plan.num_new)[plan.samples] * 13)
+                   % 32000).astype(np.int32)
+        sched.update(sampled)
+        steps += 1
+        tokens += int(plan.num_new.sum())
+        preempted += len(plan.preempted)
+    el = time.perf_counter() - t0
+    r = {"requests": 256, "steps": steps, "tokens_scheduled": tokens, "preemptions": preempted,
+         "prefix_hit_blocks": alloc.prefix_cache_stats()["hit_blocks"],
+         "us_per_step": round(el / max(steps, 1) * 1e6, 1),
+         "what": "host-only scheduler loop (schedule, plan copy-out, update) over a seeded stream; "
+                 "pool 40% of the blocks the requests would hold together; budget 2048 tokens"}
+    log("scheduler: %d steps, %d tokens, %d preemptions, %.1f us per step"
+        % (steps, tokens, preempted, r["us_per_step"]))
+    return r
+
+
 def stream_leg(dev):
     """What plain streaming reaches on this GPU, as the practical ceiling
     beside the decode roofline: the library's streaming-read kernel over
@@ -400,6 +453,7 @@ def main():
     prefill = None if args.no_prefill else prefill_leg(args, dev)
     shared = None if args.no_shared else shared_leg(args, dev)
     stream = None if args.no_stream else stream_leg(dev)
+    scheduler = scheduler_leg()
 
     # ------------------------------------------------------- CPU oracle leg
     cpu = None
@@ -448,6 +502,7 @@ def main():
         "shared_prefix": shared,
         "streaming": None if stream is None else dict(
             stream, split_kernel_pct_of_read=round(100 * achieved / stream["read_gbs"], 1)),
+        "scheduler": scheduler,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
