@@ -251,7 +251,7 @@ def load_traffic():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only (this build has no multi-GPU path); "
+        print("bench.py runs on one GPU only (the library has no multi-GPU path); "
               "got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
