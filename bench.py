@@ -571,6 +571,10 @@ def shared_leg(args, dev):
     dec = w.decode_seqs
     S = len(dec)
     alloc, kc, vc = build_pool(w, dev, w.num_blocks, step=True)
+    # consecutive calls cycle through pool copies, as consecutive layers
+    # would, so that the private suffixes come from HBM, not from a cache
+    # warmed by the previous call (the prefix's reuse within one call stays)
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(args.pools - 1)]
     sids = [s.seq_id for s in dec]
     maxb = w.max_blocks_per_seq()
     table, lens = alloc.block_table(sids, maxb)
@@ -589,19 +593,19 @@ def shared_leg(args, dev):
     reps = max(20, args.steps // 2)
 
     def timed(fn):
-        for _ in range(5):
-            fn()
+        for r in range(5):
+            fn(*pools[r % len(pools)])
         e0, e1 = hip.create(), hip.create()
         hip.record(e0, sh)
-        for _ in range(reps):
-            fn()
+        for r in range(reps):
+            fn(*pools[r % len(pools)])
         hip.record(e1, sh)
         torch.cuda.synchronize()
         return hip.elapsed_us(e0, e1) / reps
 
-    plain = timed(lambda: pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws))
-    shared = timed(lambda: pkv.decode_shared_prefix(out, q, kc, vc, d_table, d_lens, prefix_blocks,
-                                                    w.scale, wsp))
+    plain = timed(lambda kc, vc: pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws))
+    shared = timed(lambda kc, vc: pkv.decode_shared_prefix(out, q, kc, vc, d_table, d_lens,
+                                                           prefix_blocks, w.scale, wsp))
     per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     logical = float(lens.sum()) * per_token
     unique = float(prefix_blocks * 16 + (lens - prefix_blocks * 16).sum()) * per_token

@@ -75,23 +75,26 @@ stage_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, int64_
 }
 
 // Streaming read: workgroup b reads the b-th of gridDim.x equal contiguous
-// slices with 16-byte loads, four in flight per thread, and writes one word
-// folded from what it read (so that the loads stay live).
+// slices with 16-byte non-temporal loads (as the decode reads its K/V tiles),
+// four in flight per thread, and writes one word folded from what it read
+// (so that the loads stay live).
 __global__ void __launch_bounds__(256)
 stream_read_kernel(const uint4* __restrict__ src, int64_t vecs, uint32_t* __restrict__ out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* v = reinterpret_cast<const u32x4*>(src);
   const int64_t per = (vecs + gridDim.x - 1) / gridDim.x;
   const int64_t b = per * blockIdx.x;
   const int64_t e = min(b + per, vecs);
   uint32_t acc = 0;
   for (int64_t i = b + threadIdx.x; i < e; i += 4 * 256) {
-    uint4 x[4];
+    u32x4 x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t j = i + u * 256;
-      x[u] = j < e ? src[j] : uint4{0u, 0u, 0u, 0u};
+      x[u] = j < e ? __builtin_nontemporal_load(v + j) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    for (int u = 0; u < 4; ++u) acc ^= x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
   }
   // one word per workgroup: lane 0 of wave 0 keeps its own fold
   if (threadIdx.x == 0) out[blockIdx.x] = acc;

@@ -564,7 +564,7 @@ decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
       const int64_t t = tile_ptr(u);
-      load_tile<DT, D>(buf[u], kpool + t, vpool + t, k_off, v_off);
+      load_tile<DT, D, true>(buf[u], kpool + t, vpool + t, k_off, v_off);
       __builtin_amdgcn_sched_barrier(0);
     }
     int32_t kb = 0;
@@ -574,7 +574,7 @@ decode_split_kernel(DecodeParams p) {
         step(buf[u], kb + u);
         // the next load is always issued (the last tile again past the end)
         const int64_t t = tile_ptr(kb + u + DEPTH);
-        load_tile<DT, D>(buf[u], kpool + t, vpool + t, k_off, v_off);
+        load_tile<DT, D, true>(buf[u], kpool + t, vpool + t, k_off, v_off);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
