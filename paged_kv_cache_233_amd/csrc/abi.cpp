@@ -84,8 +84,10 @@ int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const
   if (new_token_stride < (int64_t)num_kv_heads * head_dim)
     return fail(PKV_ERR_INVALID_ARG, "new_token_stride %lld < num_kv_heads*head_dim",
                 (long long)new_token_stride);
-  if (num_tokens > INT32_MAX / 2) return fail(PKV_ERR_INVALID_ARG, "too many tokens");
   const int64_t elem = dtype == PKV_F32 ? 4 : 2;
+  // one thread per 16-byte piece of K and V: the grid must stay below 2^31 threads
+  if (num_tokens * 2 * num_kv_heads * (head_dim * elem / 16) > INT32_MAX - 255)
+    return fail(PKV_ERR_INVALID_ARG, "too many tokens for one launch");
   if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) % 16 != 0 ||
       (new_token_stride * elem) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "pools, new K/V and the token stride must be 16-byte aligned");

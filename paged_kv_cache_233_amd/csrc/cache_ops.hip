@@ -22,16 +22,17 @@ reshape_and_cache_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cach
                          int64_t token_stride_vec, const int64_t* __restrict__ slots,
                          int64_t num_tokens, int64_t num_slots, int32_t num_kv_heads,
                          int32_t pieces) {
-  const int64_t per_tensor = (int64_t)num_kv_heads * pieces;
-  const int64_t per_token = 2 * per_tensor;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= num_tokens * per_token) return;
-  const int64_t t = idx / per_token;
-  int64_t r = idx - t * per_token;
+  // (32-bit index arithmetic: the grid holds fewer than 2^31 threads)
+  const uint32_t per_tensor = (uint32_t)num_kv_heads * pieces;
+  const uint32_t per_token = 2 * per_tensor;
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if ((int64_t)idx >= num_tokens * per_token) return;
+  const uint32_t t = idx / per_token;
+  uint32_t r = idx - t * per_token;
   const bool is_v = r >= per_tensor;
   if (is_v) r -= per_tensor;
-  const int32_t h = (int32_t)(r / pieces);
-  const int32_t piece = (int32_t)(r - (int64_t)h * pieces);
+  const int32_t h = (int32_t)(r / (uint32_t)pieces);
+  const int32_t piece = (int32_t)(r - (uint32_t)h * pieces);
   const int64_t slot = slots[t];
   if (slot < 0 || slot >= num_slots) return;  // padding or out-of-range: no write
   const int64_t blk = slot >> 4;

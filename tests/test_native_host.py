@@ -219,6 +219,12 @@ def test_device_entry_points_reject_bad_arguments():
     assert _raw("pkv_reshape_and_cache", 18, 16, 16, 16, 128, 16, 1, 4, 1, 128, 1, None) == pkv.ERR_INVALID_ARG
     # zero tokens is a no-op
     assert _raw("pkv_reshape_and_cache", 0, 0, 0, 0, 128, 0, 0, 4, 1, 128, 1, None) == 0
+    # more 16-byte pieces than one launch's 2^31 threads (2^25 tokens x 8 heads x 16 pieces x 2)
+    assert _raw("pkv_reshape_and_cache", 16, 16, 16, 16, 1024, 16, 1 << 25, 4, 8, 128, 1,
+                None) == pkv.ERR_INVALID_ARG
+    # stream_read: bytes not a multiple of 16, or no workgroup
+    assert _raw("pkv_stream_read", 16, 40, 16, 4, None) == pkv.ERR_INVALID_ARG
+    assert _raw("pkv_stream_read", 16, 64, 16, 0, None) == pkv.ERR_INVALID_ARG
     # decode: group of 32 query heads per KV head is not built
     assert _raw("pkv_paged_attention_decode", 16, 16, 16, 16, 16, 16, 1, 4, 1, 32, 1, 128,
                 ctypes.c_float(1.0), 1, 16, 1 << 20, None) == pkv.ERR_UNSUPPORTED
