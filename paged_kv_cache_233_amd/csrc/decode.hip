@@ -209,12 +209,17 @@ __device__ __forceinline__ void zero_rows(const DecodeParams& p, int32_t s) {
     *reinterpret_cast<uint4*>(row + e * Shape<DT, D>::kElem) = uint4{0u, 0u, 0u, 0u};
 }
 
+// Partial states whose loads the merge issues together (8 or 16 were
+// slower on sequences split over a dozen waves: 11.2 and 12.4 us against
+// 9.4 us for the merge launch).
+constexpr int kMergeBatch = 4;
+
 // Fold the partial states of sequence s, KV head g (flat tiles first..last)
 // in wave order and write the normalised output. Each lane owns 8
-// consecutive output values of one query head; the states are read four at
-// a time with their loads issued together. A wave whose range starts before
-// the sequence holds its state in its second slot, every other wave in its
-// first.
+// consecutive output values of one query head; the states are read
+// kMergeBatch at a time with their loads issued together. A wave whose
+// range starts before the sequence holds its state in its second slot,
+// every other wave in its first.
 template <int DT, int D>
 __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t first,
                                int32_t last, const WaveRanges& R) {
@@ -229,16 +234,16 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
     float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int32_t wv = w0;
     while (wv <= w1) {
-      int32_t slot[4];
+      int32_t slot[kMergeBatch];
       int cnt = 0;
-      for (; wv <= w1 && cnt < 4; ++wv) {
+      for (; wv <= w1 && cnt < kMergeBatch; ++wv) {
         if (R.empty(wv)) continue;
         slot[cnt++] = 2 * wv + (R.begin(wv) < first ? 1 : 0);
       }
-      float4 o0[4], o1[4];
-      float mk[4], lk[4];
+      float4 o0[kMergeBatch], o1[kMergeBatch];
+      float mk[kMergeBatch], lk[kMergeBatch];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kMergeBatch; ++k) {
         if (k < cnt) {
           const float* base = p.ws_partial + (int64_t)slot[k] * stride;
           o0[k] = *reinterpret_cast<const float4*>(base + e);
@@ -248,7 +253,7 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kMergeBatch; ++k) {
         if (k < cnt) {
           const float m_new = fmaxf(mx, mk[k]);
           const float so = __builtin_amdgcn_exp2f(mx - m_new);
