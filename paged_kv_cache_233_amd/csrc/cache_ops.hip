@@ -33,14 +33,19 @@ reshape_and_cache_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cach
   if (is_v) r -= per_tensor;
   const int32_t h = (int32_t)(r / (uint32_t)pieces);
   const int32_t piece = (int32_t)(r - (uint32_t)h * pieces);
+  // The source row is read before the slot is checked (it is in bounds
+  // whatever the slot), so both loads take one memory round trip; the empty
+  // asm keeps the compiler from sinking the row's load past the branch.
+  const uint4 val =
+      (is_v ? v_new : k_new)[t * token_stride_vec + (int64_t)h * pieces + piece];
   const int64_t slot = slots[t];
+  __asm__ volatile("" ::"v"(val.x), "v"(val.y), "v"(val.z), "v"(val.w), "v"(slot));
   if (slot < 0 || slot >= num_slots) return;  // padding or out-of-range: no write
   const int64_t blk = slot >> 4;
   const int64_t off = slot & 15;
-  const uint4* src = (is_v ? v_new : k_new) + t * token_stride_vec + (int64_t)h * pieces + piece;
   uint4* dst = (is_v ? v_cache : k_cache) +
                ((blk * num_kv_heads + h) * 16 + off) * pieces + piece;
-  *dst = *src;
+  *dst = val;
 }
 
 // One workgroup per copy pair; the block's K and V bytes are copied in
