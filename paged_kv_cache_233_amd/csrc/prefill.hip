@@ -827,17 +827,19 @@ constexpr int kMaxPrefixParts = 16;
 
 int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t prefix_tokens) {
-  // About one workgroup per CU: (row blocks x KV heads) x parts, each part
-  // keeping at least two 32-position tiles. With fewer workgroups than two
-  // per CU each runs eight waves over two halves of its positions, which
-  // keeps the per-wave work of 2x the parts while writing half the partial
-  // states (measured on the shared workload: 8 parts 15.2 + 5.0 us for the
-  // prefix and its fold, 16 parts 16.8 + 7.4 us).
+  // About one workgroup per two CUs: (row blocks x KV heads) x parts, each
+  // part keeping at least two 32-position tiles. With fewer workgroups than
+  // two per CU each runs eight waves over two halves of its positions. Fewer
+  // parts write fewer partial states for the fold to read, and past about
+  // half the CUs the extra parallelism no longer pays for them (the whole
+  // shared-prefix decode of 128 sequences over a 2048-token prefix: 2 parts
+  // 64.2 us, 3 parts 60.5, 4 parts 59.0, 5 parts 59.3, 8 parts 60.4,
+  // 12 parts 67.6).
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t wg_tokens = kWaves * 2 * (16 / group);
   const int64_t base = (int64_t)((num_seqs + wg_tokens - 1) / wg_tokens) * num_kv_heads;
   const int32_t tiles = (prefix_tokens + kKeys - 1) / kKeys;
-  int64_t parts = ((int64_t)num_cus() + base - 1) / base;
+  int64_t parts = ((int64_t)num_cus() + 2 * base - 1) / (2 * base);
   parts = std::min<int64_t>(parts, std::max<int32_t>(1, tiles / 2));
   if (const char* env = getenv("PKV_PREFIX_PARTS")) {  // tuning override
     const int v = atoi(env);
