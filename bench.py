@@ -11,6 +11,9 @@ HBM: the allocator plans all steps first and one copy puts their indices on
 the device before timing starts. A second leg runs the serving loop as it
 would run, the allocator planning each step inside the timed loop and the
 indices crossing PCIe every step (staged_step, reported beside it).
+Per-kernel times come from HIP events in a separate run of the same planned
+steps: event records between the kernels lengthen the step, so the wall
+time (value) is taken without them.
 Consecutive steps cycle through R copies of the KV pool, as consecutive
 layers of a model would, so every step reads its keys and values from HBM
 and not from the 256 MB last-level cache.
@@ -322,56 +325,79 @@ def main():
     alloc_us = (time.perf_counter() - h0) / total_steps * 1e6
     plan_d = plan_h.to(dev)
     torch.cuda.synchronize()
-    launch = []
-    for t in range(total_steps):
-        x = plan_d[t]
-        slots = x[:S]
-        lens = x[S:].view(torch.int32)[:S]
-        table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
-        kc, vc = pools[t % len(pools)]
-        launch.append((
-            pkv.reshape_and_cache(kc, vc, k_new, v_new, slots, stream=sh, prepare=True),
-            pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="split",
-                       prepare=True),
-            pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="merge",
-                       prepare=True)))
     ev = [tuple(hip.create() for _ in range(4)) for _ in range(total_steps)]
 
-    def step(t):
-        reshape, split, merge = launch[t]
-        e0, e1, e2, e3 = ev[t]
-        hip.record(e0, sh)
-        reshape()
-        hip.record(e1, sh)
-        split()                           # decode = split-KV kernel, then merge kernel
-        hip.record(e2, sh)
-        merge()
-        hip.record(e3, sh)
+    def resident_leg(events):
+        """Run every planned step (warm-up, then timed) with its indices in HBM:
+        reshape_and_cache, the split kernel and the merge kernel. Every run
+        replays the same plans, so it writes the same slots and reads the
+        same bytes. events: bracket every kernel with HIP events (per-kernel
+        times; the event records add gaps between the kernels, so the wall
+        time is taken from a run without them). Returns (wall seconds,
+        per-kernel event times in us or None)."""
+        launch = []
+        for t in range(total_steps):
+            x = plan_d[t]
+            slots = x[:S]
+            lens = x[S:].view(torch.int32)[:S]
+            table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
+            kc, vc = pools[t % len(pools)]
+            launch.append((
+                pkv.reshape_and_cache(kc, vc, k_new, v_new, slots, stream=sh, prepare=True),
+                pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="split",
+                           prepare=True),
+                pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="merge",
+                           prepare=True)))
 
-    for t in range(args.warmup):
-        step(t)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.warmup, total_steps):
-        step(t)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        def step(t):
+            reshape, split, merge = launch[t]
+            if not events:
+                reshape()
+                split()
+                merge()
+                return
+            e0, e1, e2, e3 = ev[t]
+            hip.record(e0, sh)
+            reshape()
+            hip.record(e1, sh)
+            split()                       # decode = split-KV kernel, then merge kernel
+            hip.record(e2, sh)
+            merge()
+            hip.record(e3, sh)
+
+        for t in range(args.warmup):
+            step(t)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(args.warmup, total_steps):
+            step(t)
+        torch.cuda.synchronize()
+        leg_wall = time.perf_counter() - t0
+        if not events:
+            return leg_wall, None
+        timed = range(args.warmup, total_steps)
+        us = {k: np.array([hip.elapsed_us(ev[t][a], ev[t][b]) for t in timed])
+              for k, (a, b) in {"reshape": (0, 1), "split": (1, 2), "merge": (2, 3),
+                                "decode": (1, 3)}.items()}
+        return leg_wall, us
+
+    # per-kernel times (with events), then the wall time (without)
+    ev_wall, us = resident_leg(True)
+    wall, _ = resident_leg(False)
     ms_per_step = wall / args.steps * 1e3
     timed = range(args.warmup, total_steps)
-    rc_us = np.array([hip.elapsed_us(ev[t][0], ev[t][1]) for t in timed])
-    split_us = np.array([hip.elapsed_us(ev[t][1], ev[t][2]) for t in timed])
-    merge_us = np.array([hip.elapsed_us(ev[t][2], ev[t][3]) for t in timed])
-    dec_us = np.array([hip.elapsed_us(ev[t][1], ev[t][3]) for t in timed])
+    rc_us, split_us, merge_us, dec_us = us["reshape"], us["split"], us["merge"], us["decode"]
     kv_bytes = np.array([ctx_tokens[t] * kv_bytes_per_token for t in timed], dtype=np.float64)
     achieved = float(kv_bytes.mean() / (split_us.mean() * 1e-6) / 1e9)
     achieved_op = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
     value = float(kv_bytes.sum() / wall / 1e9)
     tokens_per_s = S * args.steps / wall
     log("decode kernels: mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
-        "reshape_and_cache %.1f us; step %.1f us wall (indices resident); allocator %.1f us "
-        "per step on the host" % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(),
-                                   merge_us.mean(), rc_us.mean(), ms_per_step * 1e3, alloc_us))
-    del launch, plan_d
+        "reshape_and_cache %.1f us; step %.1f us wall (%.1f with events; indices resident); "
+        "allocator %.1f us per step on the host"
+        % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(), merge_us.mean(),
+           rc_us.mean(), ms_per_step * 1e3, ev_wall / args.steps * 1e6, alloc_us))
+    del plan_d
 
     # ----------------------------------- staged leg: indices cross PCIe per step
     # The serving loop as it runs: the host allocator plans step t while the
@@ -513,9 +539,9 @@ def main():
         g_bytes = float(np.sum(g_tokens[args.warmup:])) * kv_bytes_per_token
         graph = {"ms_per_step": round(g_wall / args.steps * 1e3, 4),
                  "value": round(g_bytes / g_wall / 1e9, 2), "unit": "GB/s", "steps": args.steps,
-                 "what": "the same step replayed as one HIP graph per step (index staging, "
+                 "what": "the staged step replayed as one HIP graph per step (index staging, "
                          "reshape_and_cache, split and merge kernels captured once per pool "
-                         "copy); timed after the eager run, contexts still growing"}
+                         "copy); timed after the eager runs, contexts still growing"}
         log("graph replay: step %.1f us wall, %.1f GB/s" % (g_wall / args.steps * 1e6,
                                                             graph["value"]))
 
@@ -553,13 +579,14 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
-        # one layer's kernels only: reshape_and_cache + split + merge
+        # one layer's kernels only (event times): reshape_and_cache + split + merge
         "kernel_tokens_per_s": round(S / ((rc_us.mean() + dec_us.mean()) * 1e-6), 1),
         "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
                       "decode_median": round(float(np.median(dec_us)), 2),
                       "decode_split_kernel_mean": round(float(split_us.mean()), 2),
                       "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
                       "reshape_and_cache_mean": round(float(rc_us.mean()), 2),
+                      "step_with_events": round(ev_wall / args.steps * 1e6, 2),
                       "allocator_host_us_per_step": round(alloc_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
