@@ -331,6 +331,15 @@ int pkv_stream_read(const void* src, size_t bytes, uint32_t* out, int32_t workgr
 int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, size_t* out);
 
+/* Tuning: the split-KV decode runs a fixed number of single-wave workgroups,
+ * per_cu per compute unit (default 3; 0 restores it), and splits the
+ * sequences' blocks evenly over them, so this sets how the contexts are
+ * partitioned. The result does not depend on it beyond rounding. It changes
+ * the workspace size: size workspaces after setting it (a decode given a
+ * workspace that is now too small fails with PKV_ERR_WORKSPACE). Process-wide,
+ * not thread-safe; per_cu outside [0, 32] gives PKV_ERR_INVALID_ARG. */
+int pkv_decode_set_waves_per_cu(int32_t per_cu);
+
 /* Decode attention: one query token per sequence over its paged KV
  * ["My Understanding of vLLM and PagedAttention", "3. PagedAttention CUDA
  * Kernel" and "Step 4 -- Attention Computation"]:

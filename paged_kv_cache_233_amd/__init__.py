@@ -97,6 +97,7 @@ _SIGNATURES = {
                         ctypes.c_int),
     "pkv_decode_workspace_size": ([_c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)],
                                   ctypes.c_int),
+    "pkv_decode_set_waves_per_cu": ([_c_i32], ctypes.c_int),
     "pkv_paged_attention_decode": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
                                    ctypes.c_int),
@@ -566,6 +567,12 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     _check(library().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                      _dev(pairs, "pairs", torch.int64), n, nb, hkv, d,
                                      _dtype_code(k_cache), _stream(stream)))
+
+
+def decode_set_waves_per_cu(per_cu: int) -> None:
+    """Single-wave workgroups per CU of the split-KV decode (0 = default);
+    size decode workspaces after changing it."""
+    _check(library().pkv_decode_set_waves_per_cu(int(per_cu)))
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:

@@ -148,6 +148,13 @@ int pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return PKV_OK;
 }
 
+int pkv_decode_set_waves_per_cu(int32_t per_cu) {
+  pkv::clear_error();
+  if (per_cu < 0 || per_cu > 32) return fail(PKV_ERR_INVALID_ARG, "waves per CU %d outside [0, 32]", per_cu);
+  pkv::decode_set_waves_per_cu(per_cu);
+  return PKV_OK;
+}
+
 namespace {
 
 int decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,

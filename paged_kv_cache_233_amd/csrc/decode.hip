@@ -611,6 +611,7 @@ decode_merge_kernel(DecodeParams p) {
 
 int g_waves_device = -1;
 int g_waves = 0;
+int g_waves_per_cu = 0;   // set by decode_set_waves_per_cu; 0 = default
 
 int g_depth = 0;
 
@@ -662,6 +663,11 @@ hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
 
 namespace pkv {
 
+void decode_set_waves_per_cu(int per_cu) {
+  g_waves_per_cu = per_cu;
+  g_waves_device = -1;   // recomputed on the next call
+}
+
 int decode_num_waves() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -676,6 +682,7 @@ int decode_num_waves() {
       int v = atoi(env);
       if (v >= 1 && v <= 32) per_cu = v;
     }
+    if (g_waves_per_cu > 0) per_cu = g_waves_per_cu;
     int w = prop.multiProcessorCount * per_cu;
     w = (w + kXcds - 1) / kXcds * kXcds;
     g_waves = w;

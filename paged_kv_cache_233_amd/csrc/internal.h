@@ -65,6 +65,9 @@ struct DecodeArgs {
 // Number of waves the split-KV decode kernel is launched with on the current
 // device (a multiple of 8), and the workspace it needs.
 int decode_num_waves();
+// Waves per CU of the split-KV decode (0 = the default); takes effect on the
+// next call that sizes or launches a decode.
+void decode_set_waves_per_cu(int per_cu);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim);
 // phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.

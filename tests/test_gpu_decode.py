@@ -267,6 +267,39 @@ def test_decode_full_size_sampled(name):
     assert to_numpy_storage(nat["v_cache"][kb]).tobytes() == ora["v_cache"][blocks].tobytes()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_decode_independent_of_split(dtype, d):
+    """The split-KV partition (set by the decode's wave count: 1, 3 or 8
+    waves per CU, so one sequence's blocks fall into 1 to dozens of pieces)
+    changes only the rounding: every partition matches the oracle, and a
+    context held by one wave in every partition is bit-identical."""
+    _announce("decode split independence %s d=%d" % (dtype, d))
+    w = workloads.custom("split", 35, [5000, 17, 900, 2048, 1, 3100, 40], num_q_heads=8,
+                         num_kv_heads=2, head_dim=d, dtype=dtype)
+    nat = run_native(w, prefill=False)
+    ora = run_oracle(w, prefill=False)
+    dec = w.decode_seqs
+    q = torch.cat([w.seq_q(s) for s in dec]).cuda()
+    table = torch.from_numpy(nat["decode_table"]).cuda()
+    lens = torch.from_numpy(nat["decode_lens"]).cuda()
+    outs = {}
+    try:
+        for per_cu in (1, 3, 8):
+            pkv.decode_set_waves_per_cu(per_cu)
+            ws = pkv.decode_workspace(len(dec), 8, 2, d)
+            out = torch.empty_like(q)
+            pkv.decode(out, q, nat["k_cache"], nat["v_cache"], table, lens, w.scale, ws)
+            torch.cuda.synchronize()
+            assert_close(out, ora["decode"], dtype, "split per_cu=%d" % per_cu)
+            outs[per_cu] = out.cpu()
+    finally:
+        pkv.decode_set_waves_per_cu(0)
+    # the single-token sequence (index 4) is one tile, always held by one wave
+    for per_cu in (3, 8):
+        assert torch.equal(outs[1][4], outs[per_cu][4])
+        assert torch.equal(outs[1][4].float(), torch.from_numpy(ora["decode"][4]).float())
+
+
 def test_decode_phases_equal_whole_call():
     """The split-KV kernel then the merge kernel, called apart, give exactly
     the one-call result."""

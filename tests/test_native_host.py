@@ -35,6 +35,16 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= set(pkv._SIGNATURES)
 
 
+def test_decode_waves_setter_checks_its_argument():
+    """Host-only: out-of-range values are refused, 0 restores the default."""
+    with pytest.raises(pkv.Error) as e:
+        pkv.decode_set_waves_per_cu(33)
+    assert e.value.code == pkv.ERR_INVALID_ARG
+    with pytest.raises(pkv.Error):
+        pkv.decode_set_waves_per_cu(-1)
+    pkv.decode_set_waves_per_cu(0)
+
+
 def test_error_strings():
     lib = pkv.library()
     assert lib.pkv_strerror(0) == b"ok"
