@@ -124,6 +124,18 @@ def test_prefill_many_chunks():
     assert_close(nat["prefill"], ora["prefill"], "bf16", "many chunks")
 
 
+def test_prefill_chunks_at_the_cache_range_ends():
+    """512-query chunks over 0, 16, 4095 and 4096 cached tokens: the ends of
+    the mixed workload's cached range, one of them mid-block."""
+    chunks = [(0, 512), (16, 512), (4095, 512), (4096, 512)]
+    w = workloads.custom("pfe", 55, [], chunks=chunks, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    _announce("prefill chunks at cached 0/16/4095/4096")
+    nat = run_native(w)
+    ora = run_oracle(w)
+    assert_close(nat["prefill"], ora["prefill"], "bf16", "range ends")
+
+
 def test_prefill_full_mixed_workload():
     """The mixed workload's two 512-query chunks, launched as the step does."""
     w = workloads.named("mixed")
