@@ -443,3 +443,49 @@ def test_stream_read_folds_what_it_reads():
         for j in range(lo, hi, 256):
             acc ^= np.bitwise_xor.reduce(host[j])
         assert got[b] == acc, b
+
+
+# ------------------------------------------------------ random small shapes
+def _random_workload(seed: int):
+    """A seeded small workload of random shape: dtype, head_dim, KV heads,
+    group size, sequence count and lengths (zeros and block edges
+    included), sometimes a shared prefix, sometimes prefill chunks."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["f32", "bf16"][int(rng.integers(2))]
+    d = [64, 128][int(rng.integers(2))]
+    hkv = [1, 2, 4, 8][int(rng.integers(4))]
+    group = [1, 2, 3, 4, 8, 16][int(rng.integers(6))]
+    n = int(rng.integers(1, 13))
+    edge = [0, 1, 15, 16, 17, 32, 33]
+    ctx = [int(edge[rng.integers(len(edge))]) if rng.random() < 0.3 else int(rng.integers(1, 700))
+           for _ in range(n)]
+    prefix = 0
+    if rng.random() < 0.3:
+        prefix = int(rng.integers(1, 100))
+        ctx = [prefix + 1 + int(rng.integers(0, 300)) for _ in range(n)]
+    chunks = [(int(rng.integers(0, 300)), int(rng.integers(1, 80)))
+              for _ in range(int(rng.integers(0, 3)))]
+    return workloads.custom("rand%d" % seed, 2000 + seed, ctx, num_q_heads=hkv * group,
+                            num_kv_heads=hkv, head_dim=d, dtype=dtype, shared_prefix=prefix,
+                            chunks=chunks)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_small_shapes(seed):
+    """Seeded random shapes through the whole step (allocator, copy-on-write,
+    reshape_and_cache, decode, prefill): pools bit-exact, outputs within the
+    tolerance of the oracle."""
+    w = _random_workload(seed)
+    _announce("random %d: %s d=%d hq=%d hkv=%d ctx=%s chunks=%s" % (
+        seed, w.dtype, w.head_dim, w.num_q_heads, w.num_kv_heads,
+        [s.total for s in w.decode_seqs], [(s.cached, s.new_tokens) for s in w.chunk_seqs]))
+    nat = run_native(w)
+    ora = run_oracle(w)
+    assert nat["cow_pairs"] == ora["cow_pairs"]
+    assert np.array_equal(nat["step_slots"], ora["step_slots"])
+    assert to_numpy_storage(nat["k_cache"]).tobytes() == ora["k_cache"].tobytes()
+    assert to_numpy_storage(nat["v_cache"]).tobytes() == ora["v_cache"].tobytes()
+    if w.decode_seqs:
+        assert_close(nat["decode"], ora["decode"], w.dtype, "random %d decode" % seed)
+    if w.chunk_seqs:
+        assert_close(nat["prefill"], ora["prefill"], w.dtype, "random %d prefill" % seed)
