@@ -489,3 +489,18 @@ def test_random_small_shapes(seed):
         assert_close(nat["decode"], ora["decode"], w.dtype, "random %d decode" % seed)
     if w.chunk_seqs:
         assert_close(nat["prefill"], ora["prefill"], w.dtype, "random %d prefill" % seed)
+
+
+def test_decode_thousands_of_short_sequences():
+    """2000 sequences of 1-40 tokens: the lengths are scanned in many chunks
+    of 64 sequences, and rounds are cut by the piece limit, not the tile
+    limit."""
+    lens = [int(x) for x in np.random.default_rng(36).integers(1, 41, size=2000)]
+    w = workloads.custom("short", 36, lens, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         dtype="bf16")
+    _announce("decode 2000 short sequences")
+    nat = run_native(w, prefill=False)
+    ora = run_oracle(w, prefill=False)
+    _check_tables(nat, ora)
+    assert to_numpy_storage(nat["k_cache"]).tobytes() == ora["k_cache"].tobytes()
+    assert_close(nat["decode"], ora["decode"], "bf16", "2000 short")

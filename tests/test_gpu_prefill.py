@@ -136,6 +136,17 @@ def test_prefill_chunks_at_the_cache_range_ends():
     assert_close(nat["prefill"], ora["prefill"], "bf16", "range ends")
 
 
+def test_prefill_long_chunk():
+    """One 1536-query chunk over 700 cached tokens (48 row blocks of 32
+    tokens at group 4) beside a short one."""
+    w = workloads.custom("pfl", 56, [], chunks=[(700, 1536), (5, 9)], num_q_heads=8,
+                         num_kv_heads=2, head_dim=128, dtype="bf16")
+    _announce("prefill 1536-query chunk")
+    nat = run_native(w)
+    ora = run_oracle(w)
+    assert_close(nat["prefill"], ora["prefill"], "bf16", "long chunk")
+
+
 def test_prefill_full_mixed_workload():
     """The mixed workload's two 512-query chunks, launched as the step does."""
     w = workloads.named("mixed")
