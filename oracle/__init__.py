@@ -1,7 +1,7 @@
 """CPU oracle for the paged KV-cache attention path.
 
-TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check of the graft
-entry point and the bench's CPU-baseline leg may import anything here. The
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()``
+and the bench's CPU-baseline leg may import anything here. The
 product path (the HIP library and its Python binding) never imports, calls or
 falls back to this package, and this package imports nothing from the product.
 
