@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-staged", action="store_true",
                     help="skip the leg that stages the indices from pinned host memory inside "
                          "each step (PCIe-inclusive)")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="skip the leg that times the mixed workload's whole step (one and two streams)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the leg that replays the whole step as one HIP graph")
     ap.add_argument("--stage", choices=["kernel", "dma", "mapped"], default="kernel",
@@ -546,6 +548,7 @@ def main():
                                                             graph["value"]))
 
     prefill = None if args.no_prefill else prefill_leg(args, dev)
+    mixed = None if (args.no_prefill or args.no_mixed) else mixed_leg(args, dev)
     shared = None if args.no_shared else shared_leg(args, dev)
     stream = None if args.no_stream else stream_leg(dev)
     scheduler = scheduler_leg()
@@ -598,6 +601,7 @@ def main():
         "staged_step": staged,
         "graph_step": graph,
         "prefill": prefill,
+        "mixed_step": mixed,
         "shared_prefix": shared,
         "streaming": None if stream is None else dict(
             stream, split_kernel_pct_of_read=round(100 * achieved / stream["read_gbs"], 1)),
@@ -777,6 +781,96 @@ def prefill_leg(args, dev):
             "algorithmic_gflop": round(flops / 1e9, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+
+
+def mixed_leg(args, dev):
+    """The mixed workload's whole step, all inputs resident: reshape_and_cache
+    of its 1040 new tokens (16 decode tokens, two 512-query chunks), then the
+    decode of the 16 sequences and the chunked prefill of the two chunks.
+    Timed with the two attention calls one after the other on one stream, and
+    with the prefill on a second stream beside the decode (they read disjoint
+    sequences of the same pools, HBM-bound and MFMA-bound work side by side).
+    Pool copies are cycled as in the decode leg."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    w = workloads.named("mixed")
+    dec, ch = w.decode_seqs, w.chunk_seqs
+    alloc, kc0, vc0 = build_pool(w, dev, w.num_blocks)
+    ids, ns = w.step_appends()
+    slots, pairs = alloc.batch_append(ids, ns)
+    assert not pairs
+    specs = {s.seq_id: s for s in w.seqs}
+    ks, vs = [], []
+    for sid in ids:
+        k, v = w.seq_kv(specs[sid])
+        ks.append(k[specs[sid].cached:specs[sid].total])
+        vs.append(v[specs[sid].cached:specs[sid].total])
+    k_new, v_new = torch.cat(ks).to(dev), torch.cat(vs).to(dev)
+    d_slots = torch.from_numpy(slots).to(dev)
+    maxb = w.max_blocks_per_seq()
+    dt, dl = alloc.block_table([s.seq_id for s in dec], maxb)
+    pt, pl = alloc.block_table([s.seq_id for s in ch], maxb)
+    d_table, d_lens = torch.from_numpy(dt).to(dev), torch.from_numpy(dl).to(dev)
+    p_table, p_lens = torch.from_numpy(pt).to(dev), torch.from_numpy(pl).to(dev)
+    qs = [w.seq_q(s) for s in ch]
+    cu = np.cumsum([0] + [x.shape[0] for x in qs]).astype(np.int32)
+    p_cu = torch.from_numpy(cu).to(dev)
+    qmax = int(max(x.shape[0] for x in qs))
+    q_dec = torch.cat([w.seq_q(s) for s in dec]).to(dev)
+    q_pf = torch.cat(qs).to(dev)
+    out_d, out_p = torch.empty_like(q_dec), torch.empty_like(q_pf)
+    ws = pkv.decode_workspace(len(dec), w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.pools - 1)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()          # default priority
+    ready = [torch.cuda.Event() for _ in pools]
+    done = [torch.cuda.Event() for _ in pools]
+
+    def step(t, concurrent):
+        i = t % len(pools)
+        kc, vc = pools[i]
+        pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots, stream=main)
+        if concurrent:
+            ready[i].record(main)
+            side.wait_event(ready[i])
+            pkv.prefill_chunk(out_p, q_pf, p_cu, p_lens, p_table, kc, vc, qmax, w.scale,
+                              stream=side)
+            pkv.decode(out_d, q_dec, kc, vc, d_table, d_lens, w.scale, ws, stream=main)
+            done[i].record(side)
+            main.wait_event(done[i])
+        else:
+            pkv.decode(out_d, q_dec, kc, vc, d_table, d_lens, w.scale, ws, stream=main)
+            pkv.prefill_chunk(out_p, q_pf, p_cu, p_lens, p_table, kc, vc, qmax, w.scale,
+                              stream=main)
+
+    res = {}
+    for concurrent in (False, True):
+        for t in range(args.warmup):
+            step(t, concurrent)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(args.steps):
+            step(t, concurrent)
+        torch.cuda.synchronize()
+        res[concurrent] = (time.perf_counter() - t0) / args.steps * 1e6
+    kv = float(dl.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    ntok = len(dec) + int(cu[-1])
+    log("mixed step (reshape_and_cache of %d tokens, decode of %d seqs, prefill of %d chunks): "
+        "%.1f us one stream, %.1f us with the prefill on a second stream"
+        % (ntok, len(dec), len(ch), res[False], res[True]))
+    return {"workload": "mixed: %d decode seqs (ctx U[512,8192]) + %d chunks of 512 queries over %s "
+                        "cached tokens; reshape_and_cache of the %d new tokens first"
+                        % (len(dec), len(ch), [s.cached for s in ch], ntok),
+            "one_stream_us": round(res[False], 2), "two_streams_us": round(res[True], 2),
+            "speedup": round(res[False] / res[True], 3),
+            "tokens_per_s": round(ntok / (res[True] * 1e-6), 1),
+            "decode_kv_bytes": int(kv),
+            "what": "the whole step with inputs resident; two_streams: the prefill on a second "
+                    "stream (default priority) beside the decode, joined by events"}
 
 
 def cpu_baseline(w, nseq):
