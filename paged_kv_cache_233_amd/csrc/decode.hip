@@ -27,6 +27,7 @@
 // straight into registers and runs the MFMA tile step of tile_attn.h; the G
 // query heads of the group fill G of the 16 MFMA columns, the other columns
 // carry zero queries and are never stored.
+#include <atomic>
 #include <cstdlib>
 
 #include "internal.h"
@@ -609,22 +610,24 @@ decode_merge_kernel(DecodeParams p) {
   merge_sequence<DT, D>(p, s, g, first, last, R);
 }
 
-int g_waves_device = -1;
-int g_waves = 0;
-int g_waves_per_cu = 0;   // set by decode_set_waves_per_cu; 0 = default
-
-int g_depth = 0;
+// Launch settings, read by every decode call and possibly from several host
+// threads: atomics. The wave count is cached per device (0 = not known yet).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_waves[kMaxDevices];
+std::atomic<int> g_waves_per_cu{0};   // set by decode_set_waves_per_cu; 0 = default
+std::atomic<int> g_depth{0};
 
 int decode_depth() {
-  if (g_depth == 0) {
-    int d = 2;
+  int d = g_depth.load(std::memory_order_relaxed);
+  if (d == 0) {
+    d = 2;
     if (const char* env = getenv("PKV_DECODE_DEPTH")) {
       int v = atoi(env);
       if (v == 2 || v == 4 || v == 8) d = v;
     }
-    g_depth = d;
+    g_depth.store(d, std::memory_order_relaxed);
   }
-  return g_depth;
+  return d;
 }
 
 // Dynamic LDS of the split kernel: tile list, pieces, query rows.
@@ -664,14 +667,16 @@ hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
 namespace pkv {
 
 void decode_set_waves_per_cu(int per_cu) {
-  g_waves_per_cu = per_cu;
-  g_waves_device = -1;   // recomputed on the next call
+  g_waves_per_cu.store(per_cu, std::memory_order_relaxed);
+  for (auto& w : g_waves) w.store(0, std::memory_order_relaxed);   // recomputed on the next call
 }
 
 int decode_num_waves() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (dev != g_waves_device) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  const int cached = dev < kMaxDevices ? g_waves[dev].load(std::memory_order_relaxed) : 0;
+  if (cached > 0) return cached;
+  {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
     // Three single-wave workgroups per CU: with non-temporal tile loads the
@@ -682,13 +687,13 @@ int decode_num_waves() {
       int v = atoi(env);
       if (v >= 1 && v <= 32) per_cu = v;
     }
-    if (g_waves_per_cu > 0) per_cu = g_waves_per_cu;
+    const int set = g_waves_per_cu.load(std::memory_order_relaxed);
+    if (set > 0) per_cu = set;
     int w = prop.multiProcessorCount * per_cu;
     w = (w + kXcds - 1) / kXcds * kXcds;
-    g_waves = w;
-    g_waves_device = dev;
+    if (dev < kMaxDevices) g_waves[dev].store(w, std::memory_order_relaxed);
+    return w;
   }
-  return g_waves;
 }
 
 // Workspace: [block-count prefix sums, num_seqs + 1 int32, padded to 256 B]

@@ -26,6 +26,7 @@
 //
 // f32 (prefill_kernel): each wave loads its own K/V tiles in MFMA register
 // layout and runs the 16-token tile step shared with decode.
+#include <atomic>
 #include <cstdlib>
 #include <utility>
 
@@ -709,32 +710,34 @@ prefill_lds_kernel(LdsParams lp) {
   }
 }
 
-int g_ng = 0;
+// Launch settings read by every call, possibly from several host threads:
+// atomics; the CU count is cached per device (0 = not known yet).
+std::atomic<int> g_ng{0};
 
 int prefill_groups() {
-  if (g_ng == 0) {
-    int v = 2;
+  int v = g_ng.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = 2;
     if (const char* env = getenv("PKV_PREFILL_GROUPS")) {
       int e = atoi(env);
       if (e == 1 || e == 2) v = e;
     }
-    g_ng = v;
+    g_ng.store(v, std::memory_order_relaxed);
   }
-  return g_ng;
+  return v;
 }
 
-int g_num_cus = 0;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
 
 int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      g_num_cus = v;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices && (v = g_num_cus[dev].load(std::memory_order_relaxed)) > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  if (dev < kMaxDevices) g_num_cus[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 template <int D, int NG, int SPLIT>
