@@ -64,6 +64,8 @@ def parse():
                          "each step (PCIe-inclusive)")
     ap.add_argument("--no-mixed", action="store_true",
                     help="skip the leg that times the mixed workload's whole step (one and two streams)")
+    ap.add_argument("--no-cache-ops", action="store_true",
+                    help="skip the leg that times reshape_and_cache and copy_blocks alone")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the leg that replays the whole step as one HIP graph")
     ap.add_argument("--stage", choices=["kernel", "dma", "mapped"], default="kernel",
@@ -549,6 +551,7 @@ def main():
 
     prefill = None if args.no_prefill else prefill_leg(args, dev)
     mixed = None if (args.no_prefill or args.no_mixed) else mixed_leg(args, dev)
+    cache_ops = None if args.no_cache_ops else cache_ops_leg(dev)
     shared = None if args.no_shared else shared_leg(args, dev)
     stream = None if args.no_stream else stream_leg(dev)
     scheduler = scheduler_leg()
@@ -602,6 +605,7 @@ def main():
         "graph_step": graph,
         "prefill": prefill,
         "mixed_step": mixed,
+        "cache_ops": cache_ops,
         "shared_prefix": shared,
         "streaming": None if stream is None else dict(
             stream, split_kernel_pct_of_read=round(100 * achieved / stream["read_gbs"], 1)),
@@ -781,6 +785,61 @@ def prefill_leg(args, dev):
             "algorithmic_gflop": round(flops / 1e9, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+
+
+def cache_ops_leg(dev):
+    """reshape_and_cache and copy_blocks alone at the llama shapes (8 KV heads,
+    head_dim 128, bf16): bursts of 100 back-to-back launches between one pair
+    of HIP events (so the events add nothing per launch), pools of 13,000
+    blocks. reshape_and_cache: 64 tokens (one decode step) and 1040 tokens
+    (the mixed step), random distinct slots. copy_blocks: 64 pairs of
+    distinct random blocks. Bytes moved = read + written."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+
+    nb, hkv, d = 13000, 8, 128
+    gen = torch.Generator().manual_seed(77)
+    kc = torch.randn((nb, hkv, 16, d), generator=gen).to(torch.bfloat16).to(dev)
+    vc = torch.randn((nb, hkv, 16, d), generator=gen).to(torch.bfloat16).to(dev)
+    rng = np.random.default_rng(77)
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.create(), hip.create()
+    reps = 100
+
+    def burst(call):
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        hip.record(e0, sh)
+        for _ in range(reps):
+            call()
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        return hip.elapsed_us(e0, e1) / reps
+
+    res = {}
+    for t in (64, 1040):
+        slots = torch.from_numpy(rng.permutation(nb * 16)[:t].astype(np.int64)).to(dev)
+        k_new = torch.randn((t, hkv, d), generator=gen).to(torch.bfloat16).to(dev)
+        v_new = torch.randn((t, hkv, d), generator=gen).to(torch.bfloat16).to(dev)
+        call = pkv.reshape_and_cache(kc, vc, k_new, v_new, slots, stream=sh, prepare=True)
+        us = burst(call)
+        moved = 2 * 2 * t * hkv * d * 2
+        res["reshape_and_cache_%d_tokens" % t] = {"us": round(us, 2),
+                                                   "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
+    ids = rng.permutation(np.arange(1, nb))[:128]
+    pairs = torch.from_numpy(np.stack([ids[:64], ids[64:]], axis=1).astype(np.int64)).to(dev)
+    us = burst(pkv.copy_blocks(kc, vc, pairs, stream=sh, prepare=True))
+    moved = 2 * 2 * 64 * hkv * 16 * d * 2
+    res["copy_blocks_64_pairs"] = {"us": round(us, 2), "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
+    log("cache ops: " + ", ".join("%s %.1f us (%.0f GB/s)" % (k, v["us"], v["gbs"])
+                                  for k, v in res.items()))
+    res["what"] = ("bursts of 100 launches between one pair of HIP events, llama shapes; GB/s on "
+                   "bytes read + written")
+    return res
 
 
 def mixed_leg(args, dev):

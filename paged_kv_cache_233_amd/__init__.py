@@ -559,14 +559,14 @@ def stream_read(src, out, workgroups: int, stream=None, prepare=False):
                                             _stream(stream)), (src, out), prepare)
 
 
-def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+def copy_blocks(k_cache, v_cache, pairs, stream=None, prepare=False):
     """For each row (src, dst) of pairs (int64 [n, 2]), copy block src to dst."""
     torch = _torch()
     nb, hkv, d = _pool_shape(k_cache)
     n = int(pairs.numel() // 2)
-    _check(library().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                                     _dev(pairs, "pairs", torch.int64), n, nb, hkv, d,
-                                     _dtype_code(k_cache), _stream(stream)))
+    return _run(library().pkv_copy_blocks, (
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs", torch.int64), n, nb,
+        hkv, d, _dtype_code(k_cache), _stream(stream)), (k_cache, v_cache, pairs), prepare)
 
 
 def decode_set_waves_per_cu(per_cu: int) -> None:
