@@ -226,14 +226,13 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
 
 // Workspace of the shared-prefix decode: the decode workspace, then the
 // prefix states (parts x num_seqs x num_q_heads x (head_dim + 4) floats),
-// then the folded state (num_seqs x num_q_heads x (head_dim + 4) floats).
+// which the decode folds at each sequence's first piece.
 static size_t shared_prefix_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t prefix_blocks, int32_t* parts) {
   const size_t dec = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
                       255) / 256 * 256;
   *parts = pkv::prefix_state_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks * 16);
-  // per-part states, then the folded state (one per query row)
-  return dec + ((size_t)*parts + 1) * num_seqs * num_q_heads * (head_dim + 4) * 4;
+  return dec + (size_t)*parts * num_seqs * num_q_heads * (head_dim + 4) * 4;
 }
 
 int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -294,14 +293,10 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
   hipError_t err = pkv::launch_prefix_state(pa, prefix_blocks * 16, parts, state,
                                             (hipStream_t)stream);
   if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix phase launch");
-  const int64_t rows = (int64_t)num_seqs * num_q_heads;
-  float* folded = state + (int64_t)parts * rows * (head_dim + 4);
-  err = pkv::launch_prefix_fold(state, parts, rows, head_dim, folded, (hipStream_t)stream);
-  if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix fold launch");
   pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                     max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                     workspace};
-  err = pkv::launch_decode_after_prefix(a, prefix_blocks, folded, 1, 3, (hipStream_t)stream);
+  err = pkv::launch_decode_after_prefix(a, prefix_blocks, state, parts, 3, (hipStream_t)stream);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
 }
 

@@ -110,9 +110,5 @@ int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t prefix_tokens);
 hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int32_t parts,
                                float* state, hipStream_t stream);
-// Second phase: the `parts` states of each of `rows` query rows folded into
-// one, folded[row][D+4] in the same layout (parts <= 16).
-hipError_t launch_prefix_fold(const float* state, int32_t parts, int64_t rows, int32_t head_dim,
-                              float* folded, hipStream_t stream);
 
 }  // namespace pkv

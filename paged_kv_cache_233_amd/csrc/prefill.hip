@@ -833,11 +833,11 @@ int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   // About one workgroup per two CUs: (row blocks x KV heads) x parts, each
   // part keeping at least two 32-position tiles. With fewer workgroups than
   // two per CU each runs eight waves over two halves of its positions. Fewer
-  // parts write fewer partial states for the fold to read, and past about
-  // half the CUs the extra parallelism no longer pays for them (the whole
-  // shared-prefix decode of 128 sequences over a 2048-token prefix: 2 parts
-  // 64.2 us, 3 parts 60.5, 4 parts 59.0, 5 parts 59.3, 8 parts 60.4,
-  // 12 parts 67.6).
+  // parts leave fewer partial states for the decode to fold at each
+  // sequence's start, and past about half the CUs the extra parallelism no
+  // longer pays for them (the whole shared-prefix decode of 128 sequences
+  // over a 2048-token prefix: 2 parts 58.6 us, 3 parts 56.7, 4 parts 56.9,
+  // 6 parts 61.2, 8 parts 64.6).
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t wg_tokens = kWaves * 2 * (16 / group);
   const int64_t base = (int64_t)((num_seqs + wg_tokens - 1) / wg_tokens) * num_kv_heads;
@@ -877,72 +877,6 @@ hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int3
   p.state_part_stride = (int64_t)a.total_q * a.num_q_heads * (a.head_dim + 4);
   if (a.dtype != PKV_BF16) return hipErrorInvalidValue;
   return a.head_dim == 128 ? launch_lds<128, 2>(p, stream) : launch_lds<64, 2>(p, stream);
-}
-
-namespace {
-
-// One softmax state per query row from the prefix's per-part states: with
-// M = max_k m_k and w_k = 2^(m_k - M), the sum is sum_k w_k l_k and the
-// unnormalised output sum_k w_k O_k (the same rescaling the online softmax
-// applies when it moves its reference). D/4 lanes per row, four dims each;
-// every part's loads are issued before any is used.
-template <int D>
-__global__ void __launch_bounds__(256)
-prefix_fold_kernel(const float* __restrict__ state, int64_t part_stride, int32_t parts, int64_t rows,
-                   float* __restrict__ folded) {
-  constexpr int kLanes = D / 4;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = t / kLanes;
-  const int c = (int)(t % kLanes);
-  if (row >= rows) return;
-  const float* src = state + row * (D + 4);
-  float4 o[kMaxPrefixParts];
-  float2 ml[kMaxPrefixParts];
-#pragma unroll
-  for (int k = 0; k < kMaxPrefixParts; ++k) {
-    if (k < parts) {
-      o[k] = *reinterpret_cast<const float4*>(src + k * part_stride + 4 * c);
-      ml[k] = *reinterpret_cast<const float2*>(src + k * part_stride + D);
-    }
-  }
-  float m = ml[0].x;
-#pragma unroll
-  for (int k = 1; k < kMaxPrefixParts; ++k)
-    if (k < parts) m = fmaxf(m, ml[k].x);
-  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxPrefixParts; ++k) {
-    if (k < parts) {
-      const float w = __builtin_amdgcn_exp2f(ml[k].x - m);
-      acc.x += o[k].x * w;
-      acc.y += o[k].y * w;
-      acc.z += o[k].z * w;
-      acc.w += o[k].w * w;
-      l += ml[k].y * w;
-    }
-  }
-  float* dst = folded + row * (D + 4);
-  *reinterpret_cast<float4*>(dst + 4 * c) = acc;
-  if (c == 0) *reinterpret_cast<float4*>(dst + D) = float4{m, l, 0.f, 0.f};
-}
-
-}  // namespace
-
-hipError_t launch_prefix_fold(const float* state, int32_t parts, int64_t rows, int32_t head_dim,
-                              float* folded, hipStream_t stream) {
-  if (parts < 1 || parts > kMaxPrefixParts || (head_dim != 64 && head_dim != 128))
-    return hipErrorInvalidValue;
-  const int64_t threads = rows * (head_dim / 4);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  const int64_t stride = rows * (head_dim + 4);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefix_fold_kernel<128>, grid, dim3(256), 0, stream, state, stride, parts, rows,
-                       folded);
-  else
-    hipLaunchKernelGGL(prefix_fold_kernel<64>, grid, dim3(256), 0, stream, state, stride, parts, rows,
-                       folded);
-  return hipGetLastError();
 }
 
 }  // namespace pkv
