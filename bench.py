@@ -45,6 +45,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
 # the sources the decode kernels are built from (the traffic record names their hash)
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", f)
                for f in ("decode.hip", "tile_attn.h")]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_mixed_traffic.json")
+PREFILL_SRCS = [os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", f)
+                for f in ("prefill.hip", "tile_attn.h")]
 
 
 def parse():
@@ -241,21 +244,21 @@ class HipEvents:
         return ms.value * 1e3
 
 
-def kernel_source_hash():
+def kernel_source_hash(srcs=None):
     h = hashlib.sha256()
-    for f in DECODE_SRCS:
+    for f in (srcs or DECODE_SRCS):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per decode launch from the committed counter runs, if they
-    were taken on the current decode source; else None."""
+def load_traffic(path=TRAFFIC_FILE, srcs=None, key="decode_source_sha256"):
+    """HBM bytes per launch from a committed counter record, if it was taken
+    on the current source of its kernel; else None."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("decode_source_sha256") != kernel_source_hash():
+    if rec.get(key) != kernel_source_hash(srcs):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -784,7 +787,9 @@ def prefill_leg(args, dev):
             "kernel_us": round(us, 2), "query_tokens_per_s": round(int(cu[-1]) / (us * 1e-6), 1),
             "algorithmic_gflop": round(flops / 1e9, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": load_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRCS,
+                                                 "prefill_source_sha256")}}
 
 
 def cache_ops_leg(dev):
