@@ -1,6 +1,8 @@
 """GPU parity of the shared-prefix decode (the common prefix attended once
 for all sequences, then each sequence's own blocks) against the CPU oracle
 and against the ordinary decode, through the C ABI."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -17,6 +19,7 @@ CASES = {
     "bf16 d64 group 8": dict(num_q_heads=16, num_kv_heads=2, head_dim=64, dtype="bf16"),
     "bf16 d128 group 1": dict(num_q_heads=4, num_kv_heads=4, head_dim=128, dtype="bf16"),
     "bf16 d128 group 3": dict(num_q_heads=6, num_kv_heads=2, head_dim=128, dtype="bf16"),
+    "bf16 d128 group 16": dict(num_q_heads=32, num_kv_heads=2, head_dim=128, dtype="bf16"),
 }
 SUFFIX = (1, 5, 16, 17, 100, 333, 40)
 
@@ -110,3 +113,36 @@ def test_shared_prefix_full_shared_workload_sampled():
     assert_close(out[sample], ora["decode"], "bf16", "shared sampled")
     d = (out.float() - nat["decode"].float()).abs()
     assert float(d.max()) <= 2e-2
+
+
+@pytest.mark.parametrize("parts", [1, 2, 5, 16])
+def test_shared_prefix_any_number_of_prefix_parts(parts):
+    """The prefix positions cut into 1 to 16 parts, whose softmax states the
+    decode folds at each sequence's first piece: every count matches the
+    oracle, for sequences with a suffix of their own and for one whose
+    context ends with the prefix."""
+    print("[gpu] shared prefix, %d parts" % parts, flush=True)
+    prefix = 1024
+    w = workloads.custom("spp", 71, [prefix + x for x in (1, 1, 17, 300, 2, 64)], shared_prefix=prefix,
+                         **CASES["bf16 d128 group 4"])
+    nat = run_native(w, prefill=False)
+    q, table, _ = _inputs(w, nat)
+    lens_np = nat["decode_lens"].copy()
+    lens_np[-1] = prefix                 # the last sequence: the prefix alone
+    lens = torch.from_numpy(lens_np).cuda()
+    out = torch.empty_like(q)
+    old = os.environ.get("PKV_PREFIX_PARTS")
+    os.environ["PKV_PREFIX_PARTS"] = str(parts)
+    try:
+        pkv.decode_shared_prefix(out, q, nat["k_cache"], nat["v_cache"], table, lens, prefix // 16,
+                                 w.scale)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["PKV_PREFIX_PARTS"]
+        else:
+            os.environ["PKV_PREFIX_PARTS"] = old
+    ora = run_oracle(w, prefill=False)
+    qs = to_numpy_storage(q)
+    ref = paged.decode(qs, ora["k_cache"], ora["v_cache"], ora["decode_table"], lens_np, w.scale)
+    assert_close(out, ref, "bf16", "parts %d" % parts)
