@@ -41,7 +41,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 METRIC = "paged decode attention: KV-read HBM GB/s (% of peak) + tokens/s, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama_traffic.json")
 # the sources the decode kernels are built from (the traffic record names their hash)
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_233_amd", "csrc", f)
                for f in ("decode.hip", "tile_attn.h")]
@@ -55,7 +54,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama", choices=["llama", "long", "shared", "mixed"])
+    ap.add_argument("--config", default="long", choices=["llama", "long", "shared", "mixed"],
+                    help="the headline decode workload (default: long, the largest that fits one GPU)")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side decode legs (the llama and mixed workloads' decode steps)")
     ap.add_argument("--pools", type=int, default=4, help="KV pool copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64)
@@ -251,7 +253,7 @@ def kernel_source_hash(srcs=None):
     return h.hexdigest()
 
 
-def load_traffic(path=TRAFFIC_FILE, srcs=None, key="decode_source_sha256"):
+def load_traffic(path, srcs=None, key="decode_source_sha256"):
     """HBM bytes per launch from a committed counter record, if it was taken
     on the current source of its kernel; else None."""
     try:
@@ -263,99 +265,106 @@ def load_traffic(path=TRAFFIC_FILE, srcs=None, key="decode_source_sha256"):
     return rec.get("traffic_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only (the library has no multi-GPU path); "
-              "got --gpus %d" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+SIDE_DECODE = ("llama", "mixed")
+WORKLOAD_TEXT = {
+    "llama": "llama decode: 64 seqs, ctx U[128,4096] (seeded), 32 q / 8 kv heads, head_dim 128, "
+             "bf16, 16-token blocks, random placement, 1.5x pool",
+    "long": "long decode (split-KV path): 8 seqs, ctx U[32768,131072] (seeded), 32 q / 8 kv heads, "
+            "head_dim 128, bf16, 16-token blocks, random placement, 1.5x pool",
+    "mixed": "mixed step's decode part: 16 seqs, ctx U[512,8192] (seeded), 32 q / 8 kv heads, "
+             "head_dim 128, bf16, 16-token blocks, random placement, 1.5x pool",
+    "shared": "shared decode: 128 seqs sharing one 2048-token prefix + suffix U[16,512], ordinary "
+              "decode, 32 q / 8 kv heads, head_dim 128, bf16",
+}
+
+
+class Ctx:
+    """Everything one decode workload's legs share (pools, inputs, buffers)."""
+
+
+def decode_setup(w, args, dev, legs):
+    """Allocator, pool copies and step inputs of a workload's decode legs.
+    The pool has room for one new token per sequence per step of `legs`
+    legs of warm-up + timed steps."""
     import numpy as np
     import torch
 
     import paged_kv_cache_233_amd as pkv
-    import workloads
 
-    if args.copy_probe:
-        copy_probe()
-        return
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    if args.shared_probe:
-        print(json.dumps({"shared_prefix": shared_leg(args, dev)}), flush=True)
-        return
-    w = workloads.named(args.config)
+    c = Ctx()
+    c.w = w
     dec = w.decode_seqs
-    S = len(dec)
-    extra = 3 * (args.warmup + args.steps) + 2   # resident, staged and graph legs
+    c.S = S = len(dec)
+    extra = legs * (args.warmup + args.steps) + 2
     nb = w.num_blocks + S * (extra // 16 + 2)
-    maxb = w.max_blocks_per_seq(extra)
+    c.maxb = w.max_blocks_per_seq(extra)
     dt = w.torch_dtype
-    log("workload %s: %d decode seqs, pool %d blocks, max %d blocks/seq" % (w.name, S, nb, maxb))
-
-    # ---------------------------------------------------------------- setup
-    alloc, kc0, vc0 = build_pool(w, dev, nb)
-    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.pools - 1)]
-    sids = np.array([s.seq_id for s in dec], dtype=np.int64)
-    ones = np.ones(S, dtype=np.int32)
+    log("workload %s: %d decode seqs, pool %d blocks, max %d blocks/seq" % (w.name, S, nb, c.maxb))
+    c.alloc, kc0, vc0 = build_pool(w, dev, nb)
+    c.pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.pools - 1)]
+    c.sids = np.array([s.seq_id for s in dec], dtype=np.int64)
+    c.ones = np.ones(S, dtype=np.int32)
     gen = torch.Generator().manual_seed(1234)
-    q = torch.randn((S, w.num_q_heads, w.head_dim), generator=gen).to(dt).to(dev)
-    k_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
-    v_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
-    out = torch.empty_like(q)
-    ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
+    c.q = torch.randn((S, w.num_q_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    c.k_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    c.v_new = torch.randn((S, w.num_kv_heads, w.head_dim), generator=gen).to(dt).to(dev)
+    c.out = torch.empty_like(c.q)
+    c.ws = pkv.decode_workspace(S, w.num_q_heads, w.num_kv_heads, w.head_dim, dev)
     # Per-step indices: slots (int64 [S]), then context lengths (int32 [S])
     # and the block table (int32 [S, maxb]), packed in one buffer of int64
     # words.
-    n32 = S + S * maxb
-    words = S + (n32 + 1) // 2
-    kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    hip = HipEvents()
-    pairs_buf = np.empty(2 * S, dtype=np.int64)
-    total_steps = args.warmup + args.steps
+    n32 = S + S * c.maxb
+    c.words = S + (n32 + 1) // 2
+    c.kv_bytes_per_token = 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    c.pairs_buf = np.empty(2 * S, dtype=np.int64)
+    return c
 
-    # ------------------------------------------------ headline: resident leg
-    # The host allocator plans every step first: one token appended to each
-    # sequence, the slots, lengths and block table of step t written into
-    # slice t of one pinned buffer; one copy puts all slices in HBM. The timed
-    # loop then runs reshape_and_cache, the split kernel and the merge kernel
-    # per step with every input already resident on the device.
-    plan_h = torch.empty((total_steps, words), dtype=torch.int64).pin_memory()
+
+def resident_leg(c, args, hip):
+    """The headline measurement of one workload: the host allocator plans
+    every step first (one token appended to each sequence; the slots,
+    lengths and block table of step t written into slice t of one pinned
+    buffer), one copy puts all slices in HBM, then every planned step
+    (warm-up, then timed) runs reshape_and_cache, the split kernel and the
+    merge kernel with its indices resident. The planned steps run twice with
+    the same plans (same slots written, same bytes read): once with HIP
+    events around every kernel (per-kernel times; the event records add gaps
+    between the kernels), once without (the wall time behind the value)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+
+    w, S, maxb = c.w, c.S, c.maxb
+    sh = torch.cuda.current_stream().cuda_stream
+    total_steps = args.warmup + args.steps
+    plan_h = torch.empty((total_steps, c.words), dtype=torch.int64).pin_memory()
     h0 = time.perf_counter()
     ctx_tokens = []
     for t in range(total_steps):
         base = plan_h[t].data_ptr()
-        assert alloc.batch_append_into(sids, ones, base, pairs_buf) == 0
-        alloc.fill_block_table_into(sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
+        assert c.alloc.batch_append_into(c.sids, c.ones, base, c.pairs_buf) == 0
+        c.alloc.fill_block_table_into(c.sids, base + 8 * S + 4 * S, maxb, base + 8 * S)
         ctx_tokens.append(int(plan_h[t, S:].numpy().view(np.int32)[:S].sum()))
     alloc_us = (time.perf_counter() - h0) / total_steps * 1e6
-    plan_d = plan_h.to(dev)
+    plan_d = plan_h.to(c.q.device)
     torch.cuda.synchronize()
     ev = [tuple(hip.create() for _ in range(4)) for _ in range(total_steps)]
+    launch = []
+    for t in range(total_steps):
+        x = plan_d[t]
+        slots = x[:S]
+        lens = x[S:].view(torch.int32)[:S]
+        table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
+        kc, vc = c.pools[t % len(c.pools)]
+        launch.append((
+            pkv.reshape_and_cache(kc, vc, c.k_new, c.v_new, slots, stream=sh, prepare=True),
+            pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="split",
+                       prepare=True),
+            pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="merge",
+                       prepare=True)))
 
-    def resident_leg(events):
-        """Run every planned step (warm-up, then timed) with its indices in HBM:
-        reshape_and_cache, the split kernel and the merge kernel. Every run
-        replays the same plans, so it writes the same slots and reads the
-        same bytes. events: bracket every kernel with HIP events (per-kernel
-        times; the event records add gaps between the kernels, so the wall
-        time is taken from a run without them). Returns (wall seconds,
-        per-kernel event times in us or None)."""
-        launch = []
-        for t in range(total_steps):
-            x = plan_d[t]
-            slots = x[:S]
-            lens = x[S:].view(torch.int32)[:S]
-            table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
-            kc, vc = pools[t % len(pools)]
-            launch.append((
-                pkv.reshape_and_cache(kc, vc, k_new, v_new, slots, stream=sh, prepare=True),
-                pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="split",
-                           prepare=True),
-                pkv.decode(out, q, kc, vc, table, lens, w.scale, ws, stream=sh, phase="merge",
-                           prepare=True)))
-
+    def run(events):
         def step(t):
             reshape, split, merge = launch[t]
             if not events:
@@ -379,32 +388,106 @@ def main():
         for t in range(args.warmup, total_steps):
             step(t)
         torch.cuda.synchronize()
-        leg_wall = time.perf_counter() - t0
-        if not events:
-            return leg_wall, None
-        timed = range(args.warmup, total_steps)
-        us = {k: np.array([hip.elapsed_us(ev[t][a], ev[t][b]) for t in timed])
-              for k, (a, b) in {"reshape": (0, 1), "split": (1, 2), "merge": (2, 3),
-                                "decode": (1, 3)}.items()}
-        return leg_wall, us
+        return time.perf_counter() - t0
 
-    # per-kernel times (with events), then the wall time (without)
-    ev_wall, us = resident_leg(True)
-    wall, _ = resident_leg(False)
-    ms_per_step = wall / args.steps * 1e3
+    ev_wall = run(True)
     timed = range(args.warmup, total_steps)
-    rc_us, split_us, merge_us, dec_us = us["reshape"], us["split"], us["merge"], us["decode"]
-    kv_bytes = np.array([ctx_tokens[t] * kv_bytes_per_token for t in timed], dtype=np.float64)
-    achieved = float(kv_bytes.mean() / (split_us.mean() * 1e-6) / 1e9)
-    achieved_op = float(kv_bytes.mean() / (dec_us.mean() * 1e-6) / 1e9)
-    value = float(kv_bytes.sum() / wall / 1e9)
-    tokens_per_s = S * args.steps / wall
-    log("decode kernels: mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
-        "reshape_and_cache %.1f us; step %.1f us wall (%.1f with events; indices resident); "
-        "allocator %.1f us per step on the host"
-        % (dec_us.mean(), dec_us.min(), np.median(dec_us), split_us.mean(), merge_us.mean(),
-           rc_us.mean(), ms_per_step * 1e3, ev_wall / args.steps * 1e6, alloc_us))
+    us = {k: np.array([hip.elapsed_us(ev[t][a], ev[t][b]) for t in timed])
+          for k, (a, b) in {"reshape": (0, 1), "split": (1, 2), "merge": (2, 3),
+                            "decode": (1, 3)}.items()}
+    wall = run(False)
     del plan_d
+    kv_bytes = np.array([ctx_tokens[t] * c.kv_bytes_per_token for t in timed], dtype=np.float64)
+    r = {"ctx": c, "wall": wall, "ev_wall": ev_wall, "us": us, "kv_bytes": kv_bytes,
+         "alloc_us": alloc_us, "ms_per_step": wall / args.steps * 1e3,
+         "value": float(kv_bytes.sum() / wall / 1e9),
+         "achieved": float(kv_bytes.mean() / (us["split"].mean() * 1e-6) / 1e9),
+         "achieved_op": float(kv_bytes.mean() / (us["decode"].mean() * 1e-6) / 1e9)}
+    log("%s: decode kernels mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
+        "reshape_and_cache %.1f us; step %.1f us wall (%.1f with events; indices resident) = "
+        "%.1f GB/s (%.1f%% of peak); split kernel %.1f%%; allocator %.1f us per step on the host"
+        % (w.name, us["decode"].mean(), us["decode"].min(), np.median(us["decode"]),
+           us["split"].mean(), us["merge"].mean(), us["reshape"].mean(), r["ms_per_step"] * 1e3,
+           ev_wall / args.steps * 1e6, r["value"], 100 * r["value"] / HBM_PEAK_GBS,
+           100 * r["achieved"] / HBM_PEAK_GBS, alloc_us))
+    return r
+
+
+def summary(c, r, args):
+    """The JSON fields of one workload's resident decode leg."""
+    import numpy as np
+
+    w, S, us = c.w, c.S, r["us"]
+    rc_us, split_us, merge_us, dec_us = us["reshape"], us["split"], us["merge"], us["decode"]
+    kv_bytes = r["kv_bytes"]
+    return {
+        "config": {"workload": WORKLOAD_TEXT.get(w.name, w.name), "name": w.name,
+                   "num_seqs": S,
+                   "mean_context_tokens": round(float(kv_bytes.mean() / c.kv_bytes_per_token / S), 1),
+                   "kv_bytes_per_step": int(kv_bytes.mean()), "pool_copies_cycled": len(c.pools),
+                   "index_staging": "resident: every step's slots, lengths and table copied to "
+                                    "HBM before timing",
+                   "parallelism": "single GPU"},
+        "value_gbs": round(r["value"], 2),
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "pct_of_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(S * args.steps / r["wall"], 1),
+        # one layer's kernels only (event times): reshape_and_cache + split + merge
+        "kernel_tokens_per_s": round(S / ((rc_us.mean() + dec_us.mean()) * 1e-6), 1),
+        "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
+                      "decode_median": round(float(np.median(dec_us)), 2),
+                      "decode_split_kernel_mean": round(float(split_us.mean()), 2),
+                      "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
+                      "reshape_and_cache_mean": round(float(rc_us.mean()), 2),
+                      "step_with_events": round(r["ev_wall"] / args.steps * 1e6, 2),
+                      "allocator_host_us_per_step": round(r["alloc_us"], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(decode_traffic_file(w.name)),
+                     "kernel": "decode_split_kernel (dominant kernel of paged_attention_decode)",
+                     "algorithmic_bytes_per_launch": int(kv_bytes.mean())},
+        "decode_op": {"kernels": "decode_split_kernel + decode_merge_kernel",
+                      "achieved_gbs": round(r["achieved_op"], 2),
+                      "frac_of_hbm_peak": round(r["achieved_op"] / HBM_PEAK_GBS, 4)},
+    }
+
+
+def decode_traffic_file(name):
+    return os.path.join(ROOT, "profiles", "decode_%s_traffic.json" % name)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (the library has no multi-GPU path); "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    if args.copy_probe:
+        copy_probe()
+        return
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.shared_probe:
+        print(json.dumps({"shared_prefix": shared_leg(args, dev)}), flush=True)
+        return
+    w = workloads.named(args.config)
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    ctx = decode_setup(w, args, dev, legs=3)        # resident, staged and graph legs
+    head = resident_leg(ctx, args, hip)
+    S, maxb, words, dt = ctx.S, ctx.maxb, ctx.words, w.torch_dtype
+    alloc, pools, sids, ones = ctx.alloc, ctx.pools, ctx.sids, ctx.ones
+    q, k_new, v_new, out, ws = ctx.q, ctx.k_new, ctx.v_new, ctx.out, ctx.ws
+    pairs_buf, kv_bytes_per_token = ctx.pairs_buf, ctx.kv_bytes_per_token
+    total_steps = args.warmup + args.steps
+    ms_per_step = head["ms_per_step"]
+    value = head["value"]
 
     # ----------------------------------- staged leg: indices cross PCIe per step
     # The serving loop as it runs: the host allocator plans step t while the
@@ -552,6 +635,17 @@ def main():
         log("graph replay: step %.1f us wall, %.1f GB/s" % (g_wall / args.steps * 1e6,
                                                             graph["value"]))
 
+    del ctx, pools, alloc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    side = {}
+    for name in SIDE_DECODE:
+        if name != args.config and not args.no_side:
+            c2 = decode_setup(workloads.named(name), args, dev, legs=1)
+            side[name] = summary(c2, resident_leg(c2, args, hip), args)
+            del c2
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     prefill = None if args.no_prefill else prefill_leg(args, dev)
     mixed = None if (args.no_prefill or args.no_mixed) else mixed_leg(args, dev)
     cache_ops = None if args.no_cache_ops else cache_ops_leg(dev)
@@ -577,33 +671,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s decode: %d seqs, ctx U[128,4096] (seeded), %d q / %d kv heads, "
-                               "head_dim %d, 16-token blocks, random placement, 1.5x pool"
-                               % (w.name, S, w.num_q_heads, w.num_kv_heads, w.head_dim)
-                   if w.name == "llama" else w.name,
-                   "num_seqs": S, "mean_context_tokens": round(float(kv_bytes.mean() / kv_bytes_per_token / S), 1),
-                   "kv_bytes_per_step": int(kv_bytes.mean()), "pool_copies_cycled": len(pools),
-                   "index_staging": "resident: every step's slots, lengths and table copied to "
-                                    "HBM before timing",
-                   "parallelism": "single GPU"},
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "decode_tokens_per_s": round(tokens_per_s, 1),
-        # one layer's kernels only (event times): reshape_and_cache + split + merge
-        "kernel_tokens_per_s": round(S / ((rc_us.mean() + dec_us.mean()) * 1e-6), 1),
-        "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
-                      "decode_median": round(float(np.median(dec_us)), 2),
-                      "decode_split_kernel_mean": round(float(split_us.mean()), 2),
-                      "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
-                      "reshape_and_cache_mean": round(float(rc_us.mean()), 2),
-                      "step_with_events": round(ev_wall / args.steps * 1e6, 2),
-                      "allocator_host_us_per_step": round(alloc_us, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(),
-                     "kernel": "decode_split_kernel (dominant kernel of paged_attention_decode)"},
-        "decode_op": {"kernels": "decode_split_kernel + decode_merge_kernel",
-                      "achieved_gbs": round(achieved_op, 2),
-                      "frac_of_hbm_peak": round(achieved_op / HBM_PEAK_GBS, 4)},
+    }
+    res.update(summary(head["ctx"], head, args))
+    res.update({
         "staged_step": staged,
         "graph_step": graph,
         "prefill": prefill,
@@ -611,10 +681,11 @@ def main():
         "cache_ops": cache_ops,
         "shared_prefix": shared,
         "streaming": None if stream is None else dict(
-            stream, split_kernel_pct_of_read=round(100 * achieved / stream["read_gbs"], 1)),
+            stream, split_kernel_pct_of_read=round(100 * head["achieved"] / stream["read_gbs"], 1)),
         "scheduler": scheduler,
+        "side_decode": side,
         "cpu_baseline": cpu,
-    }
+    })
     print(json.dumps(res), flush=True)
 
 
@@ -996,6 +1067,11 @@ def cpu_baseline(w, nseq):
     log("oracle: %d reps over %d seqs in %.2f s -> %.3f GB/s; %d threads: %d reps in %.2f s -> "
         "%.3f GB/s" % (reps, len(sample), el, gbs, len(parts), mreps, mel, mgbs))
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cores": {"cpu_count": os.cpu_count(),
+                           "affinity": len(os.sched_getaffinity(0)),
+                           "what": "logical CPUs of the host the oracle ran on (os.cpu_count) and "
+                                   "those this process may run on (its affinity mask); the oracle "
+                                   "used 1 (value) and threads.cores (threads)"},
             "sample": "%d of %d decode sequences of the same workload (%d context tokens), "
                       "materialise + float64 softmax attention, %d repetitions, BLAS limited to "
                       "1 thread" % (len(sample), len(dec), tokens, reps),

@@ -70,6 +70,24 @@ const char* pkv_strerror(int code);
 /* Library version, major*10000 + minor*100 + patch. */
 int pkv_version(void);
 
+/* Debug checks (off by default; on when PKV_DEBUG_CHECKS=1 is set in the
+ * environment when the library is first used, or after
+ * pkv_set_debug_checks(1)). With them on, pkv_reshape_and_cache waits for
+ * its stream, reads the slot mapping back and refuses (PKV_ERR_INVALID_ARG,
+ * nothing launched) a mapping that pkv_check_slot_mapping rejects. They
+ * synchronise with the host: not for graph capture or timed runs.
+ * Process-wide. */
+int pkv_set_debug_checks(int32_t enabled);
+/* Host check of a slot mapping held in host memory, the one the debug mode
+ * of pkv_reshape_and_cache applies: every token's new K/V has one slot of its
+ * own ["vLLM: what PagedAttention turned into", section "The problem
+ * PagedAttention was actually solving"], so PKV_ERR_INVALID_ARG (the message
+ * names the entry) for a non-negative slot that an earlier token of the same
+ * call also has, a slot in the null block 0 (never a write target, section
+ * "The block pool, and the two tricks in it") or one beyond
+ * num_blocks*16. Negative slots (padding) pass. */
+int pkv_check_slot_mapping(const int64_t* slot_mapping, int64_t num_tokens, int32_t num_blocks);
+
 /* ------------------------------------------------------------------------ */
 /* Host allocator: the KV-cache manager that allocates blocks, frees them and
  * maintains block tables ["My Understanding of vLLM and PagedAttention",
@@ -107,6 +125,15 @@ int pkv_allocator_destroy(pkv_allocator* a);
  * of 1..num_blocks-1 (n = num_blocks-1); only while no sequence exists.
  * Used to place blocks at random physical positions. */
 int pkv_allocator_set_free_order(pkv_allocator* a, const int32_t* order, int32_t n);
+/* Random physical placement from a seed ["My Understanding of vLLM and
+ * PagedAttention", section "2. Physical Blocks": a sequence's blocks need not
+ * be contiguous]: installs as the free order the ids 1..num_blocks-1,
+ * ascending, permuted by a Fisher-Yates shuffle (Durstenfeld's form: for i =
+ * n-1 down to 1, swap entries i and r % (i+1)) whose draws r are successive
+ * SplitMix64 outputs (Steele, Lea and Flood, OOPSLA 2014: a 64-bit counter
+ * starting at seed, advanced by 0x9E3779B97F4A7C15 and mixed). Same
+ * conditions and errors as pkv_allocator_set_free_order, which it calls. */
+int pkv_allocator_shuffle_free_list(pkv_allocator* a, uint64_t seed);
 /* Create an empty sequence. PKV_ERR_SEQ_EXISTS if the id is taken. */
 int pkv_seq_add(pkv_allocator* a, int64_t seq_id);
 /* Append n_tokens >= 0 tokens to one sequence. out_slots[n_tokens] receives
@@ -291,7 +318,8 @@ int pkv_scheduler_request(pkv_scheduler* s, int64_t req_id, int32_t* state, int3
  * with a stride of new_token_stride elements between tokens (>= num_kv_heads
  * *head_dim; heads and dims contiguous). slot_mapping: device int64
  * [num_tokens]. A slot < 0 or >= num_blocks*16 is skipped (no write). Two
- * tokens with the same slot in one call race (caller error). Bit-exact copy. */
+ * tokens with the same slot in one call race (caller error; refused in the
+ * debug mode, see pkv_set_debug_checks). Bit-exact copy. */
 int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                           int64_t new_token_stride, const int64_t* slot_mapping,
                           int64_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,

@@ -67,6 +67,25 @@ def block_hash(parent: Optional[bytes], tokens: Sequence[int], extra: int = 0) -
     return hashlib.sha256(msg).digest()
 
 
+def splitmix64(seed: int, n: int) -> List[int]:
+    """The first n outputs of SplitMix64 (Steele, Lea and Flood, "Fast
+    splittable pseudorandom number generators", OOPSLA 2014) from a 64-bit
+    state that starts at seed: each step adds the odd constant
+    0x9E3779B97F4A7C15 to the state and returns it mixed by
+    z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+    z *= 0x94D049BB133111EB; z ^= z >> 31 (all modulo 2^64)."""
+    mask = (1 << 64) - 1
+    state = int(seed) & mask
+    out = []
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & mask
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & mask
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & mask
+        out.append(z ^ (z >> 31))
+    return out
+
+
 class OutOfBlocks(Exception):
     pass
 
@@ -99,6 +118,19 @@ class AllocatorModel:
             raise ValueError("free order must permute 1..NB-1 while the pool is empty")
         self._clear_cache()
         self.free = collections.deque(order)
+
+    def shuffle_free_list(self, seed: int) -> None:
+        """Random physical placement from a seed: the ids 1..NB-1, ascending,
+        permuted by a Fisher-Yates shuffle (Durstenfeld's form: for i from
+        the last index down to 1, swap entry i with entry r mod (i + 1)),
+        where r are successive SplitMix64 outputs (Steele, Lea and Flood,
+        OOPSLA 2014) of a counter that starts at the seed."""
+        draws = splitmix64(seed, max(0, self.num_blocks - 2))
+        order = list(range(1, self.num_blocks))
+        for k, i in enumerate(range(len(order) - 1, 0, -1)):
+            j = draws[k] % (i + 1)
+            order[i], order[j] = order[j], order[i]
+        self.set_free_order(order)
 
     def _clear_cache(self) -> None:
         self.hash.clear()

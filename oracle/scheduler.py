@@ -7,12 +7,13 @@ Policy, from the pages (cited by page title and section):
   free their blocks, queued requests are admitted into the room that made,
   and when memory runs short a request is preempted ("(2) vLLM Internals
   ...", "2. Continuous Batching").
-* One token budget per step, no prefill or decode phase: each request only
-  has a count of tokens whose KV is computed and a count of tokens it holds.
-  The running list is walked first, each request getting the tokens it
-  needs to catch up (one, for a plain decode); then the waiting queue spends
-  what is left. A queued prompt gets min(tokens still to compute, budget
-  left), capped by a long-prefill threshold when one is set. With chunked
+* A step has a single token budget and no separate prefill and decode
+  phases; a request is described by two counters, the tokens it holds and
+  the tokens whose KV has been computed. Requests already running are
+  served first, each with the difference of its two counters (a decode
+  step needs one token); queued requests share whatever budget remains. A
+  queued prompt is granted the smaller of its uncomputed tokens and the
+  remaining budget, further capped by a long-prefill threshold if set. With chunked
   prefill switched off, a prompt that does not fit what is left stops the
   walk and waits ("vLLM: what PagedAttention turned into", "The scheduler,
   and what it has to balance now").
@@ -20,8 +21,9 @@ Policy, from the pages (cited by page title and section):
   are freed, its computed count is set to zero and it goes to the front of
   the waiting queue; a step that had to preempt admits no new request
   ("vLLM: what PagedAttention turned into", "Preemption, and the path that
-  got deleted"). Freed blocks keep their hashes, so a preempted request
-  that comes back may find its own prefix still cached (same section).
+  got deleted"). Since freeing a hashed block does not drop its hash, a
+  preempted request readmitted soon enough can reattach its own cached
+  prefix (same section).
 
 Readings where the pages are silent:
 

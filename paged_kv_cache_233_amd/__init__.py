@@ -29,6 +29,11 @@ BF16 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# The host-only build of the allocator, scheduler and hashing code with
+# address and undefined-behaviour sanitizers (build.build_host_sanitized()).
+# With PKV_HOST_SANITIZED=1 the binding loads it instead of libpkv.so; its
+# kernel entry points are absent and calling one raises AttributeError.
+HOST_SANITIZED_LIB_PATH = os.path.join(_HERE, "libpkv_host_asan.so")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -54,6 +59,9 @@ _SIGNATURES = {
     "pkv_allocator_create": ([_c_i32, ctypes.POINTER(_c_p)], ctypes.c_int),
     "pkv_allocator_destroy": ([_c_p], ctypes.c_int),
     "pkv_allocator_set_free_order": ([_c_p, _c_p, _c_i32], ctypes.c_int),
+    "pkv_allocator_shuffle_free_list": ([_c_p, ctypes.c_uint64], ctypes.c_int),
+    "pkv_set_debug_checks": ([_c_i32], ctypes.c_int),
+    "pkv_check_slot_mapping": ([_c_p, _c_i64, _c_i32], ctypes.c_int),
     "pkv_seq_add": ([_c_p, _c_i64], ctypes.c_int),
     "pkv_seq_append": ([_c_p, _c_i64, _c_i32, _c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
     "pkv_batch_append": ([_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_p], ctypes.c_int),
@@ -120,12 +128,19 @@ def library() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
+            host_only = os.environ.get("PKV_HOST_SANITIZED") == "1"
+            path = HOST_SANITIZED_LIB_PATH if host_only else LIB_PATH
+            if not os.path.exists(path):
                 from . import build as _build
-                _build.build()
-            lib = ctypes.CDLL(LIB_PATH)
+                if host_only:
+                    _build.build_host_sanitized()
+                else:
+                    _build.build()
+            lib = ctypes.CDLL(path)
             for name, (args, res) in _SIGNATURES.items():
-                fn = getattr(lib, name)
+                fn = getattr(lib, name, None) if host_only else getattr(lib, name)
+                if fn is None:
+                    continue
                 fn.argtypes = args
                 fn.restype = res
             _lib = lib
@@ -241,6 +256,10 @@ class Allocator:
     def set_free_order(self, order) -> None:
         o = np.ascontiguousarray(order, dtype=np.int32)
         _check(self._lib.pkv_allocator_set_free_order(self._h, _ptr(o), int(o.size)))
+
+    def shuffle_free_list(self, seed: int) -> None:
+        """Seeded random physical placement (see pkv_allocator_shuffle_free_list)."""
+        _check(self._lib.pkv_allocator_shuffle_free_list(self._h, int(seed) & (2 ** 64 - 1)))
 
     def add(self, sid: int) -> None:
         _check(self._lib.pkv_seq_add(self._h, int(sid)))
@@ -529,6 +548,18 @@ def reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None,
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
         _dev(v_new, "v_new"), hkv * d, _idx(slot_mapping, "slot_mapping", torch.int64), t, nb, hkv, d,
         _dtype_code(k_cache), _stream(stream)), (k_cache, v_cache, k_new, v_new, slot_mapping), prepare)
+
+
+def set_debug_checks(enabled: bool) -> None:
+    """Switch the library's debug checks (see pkv_set_debug_checks)."""
+    _check(library().pkv_set_debug_checks(1 if enabled else 0))
+
+
+def check_slot_mapping(slots, num_blocks: int) -> None:
+    """Host check of a slot mapping (numpy int64): raises Error for a repeated
+    non-negative slot, a slot in the null block or one outside the pool."""
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    _check(library().pkv_check_slot_mapping(_ptr(s) if s.size else None, int(s.size), int(num_blocks)))
 
 
 def stage_copy(dst, src, stream=None, prepare=False):

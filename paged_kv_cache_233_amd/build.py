@@ -13,7 +13,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "allocator.cpp", "scheduler.cpp", "sha256.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "errors.cpp", "allocator.cpp", "scheduler.cpp", "sha256.cpp", "cache_ops.hip",
+           "decode.hip", "prefill.hip"]
+# The host-only part (no HIP runtime): built alone, with sanitizers, by
+# build_host_sanitized().
+HOST_SOURCES = ["errors.cpp", "allocator.cpp", "scheduler.cpp", "sha256.cpp"]
+HOST_LIB = os.path.join(HERE, "libpkv_host_asan.so")
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 
 # Packed-FP32 VALU instructions are kept out of all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -47,6 +53,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host-only sources (allocator, scheduler, SHA-256, status
+    plumbing) built with g++ and AddressSanitizer + UndefinedBehaviorSanitizer
+    into libpkv_host_asan.so. A process that loads it needs the ASan runtime
+    preloaded (LD_PRELOAD of g++'s libasan.so)."""
+    with tempfile.TemporaryDirectory(prefix="pkv_host_asan_") as tmp:
+        objs = []
+        for src in HOST_SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-Wall"] + SANITIZE +
+                 ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, src),
+                  "-o", obj], verbose)
+            objs.append(obj)
+        tmp_lib = HOST_LIB + ".tmp"
+        _run(["g++", "-shared", "-fPIC"] + SANITIZE + ["-o", tmp_lib] + objs, verbose)
+        os.replace(tmp_lib, HOST_LIB)
+    return HOST_LIB
+
+
+def asan_runtime() -> str:
+    """Path of g++'s AddressSanitizer runtime (for LD_PRELOAD)."""
+    return subprocess.run(["g++", "-print-file-name=libasan.so"], stdout=subprocess.PIPE,
+                          text=True, check=True).stdout.strip()
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -63,4 +94,7 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

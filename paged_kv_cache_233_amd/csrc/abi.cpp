@@ -1,25 +1,12 @@
 // C entry points of the device kernels: argument checks on the host, then an
-// asynchronous launch on the caller's stream. Also the error-message plumbing.
+// asynchronous launch on the caller's stream.
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "internal.h"
 
 namespace pkv {
-
-namespace {
-thread_local char g_msg[512] = "";
-}
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
-  va_end(ap);
-  return code;
-}
-
-void clear_error() { g_msg[0] = '\0'; }
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -49,27 +36,22 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
   return PKV_OK;
 }
 
+// Debug mode of pkv_reshape_and_cache: waits for the stream, reads the slot
+// mapping back (device or pinned host memory) and checks it on the host
+// before launching. Not for graph capture.
+int debug_check_slots(const int64_t* slot_mapping, int64_t num_tokens, int32_t num_blocks,
+                      hipStream_t stream) {
+  std::vector<int64_t> host((size_t)num_tokens);
+  hipError_t err = hipStreamSynchronize(stream);
+  if (err == hipSuccess)
+    err = hipMemcpy(host.data(), slot_mapping, (size_t)num_tokens * sizeof(int64_t), hipMemcpyDefault);
+  if (err != hipSuccess) return pkv::hip_fail(err, "reshape_and_cache debug check (reading the slots)");
+  return pkv::check_slot_mapping(host.data(), num_tokens, num_blocks);
+}
+
 }  // namespace
 
 extern "C" {
-
-const char* pkv_last_error(void) { return pkv::g_msg; }
-
-const char* pkv_strerror(int code) {
-  switch (code) {
-    case PKV_OK: return "ok";
-    case PKV_ERR_INVALID_ARG: return "invalid argument";
-    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PKV_ERR_OUT_OF_BLOCKS: return "out of KV blocks";
-    case PKV_ERR_NO_SUCH_SEQ: return "no such sequence";
-    case PKV_ERR_SEQ_EXISTS: return "sequence exists";
-    case PKV_ERR_WORKSPACE: return "workspace too small";
-    case PKV_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-int pkv_version(void) { return 100; }
 
 int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                           int64_t new_token_stride, const int64_t* slot_mapping,
@@ -91,6 +73,9 @@ int pkv_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new, const
   if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) % 16 != 0 ||
       (new_token_stride * elem) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "pools, new K/V and the token stride must be 16-byte aligned");
+  if (pkv::debug_checks()) {
+    if (int e = debug_check_slots(slot_mapping, num_tokens, num_blocks, (hipStream_t)stream)) return e;
+  }
   hipError_t err = pkv::launch_reshape_and_cache(k_cache, v_cache, k_new, v_new, new_token_stride,
                                                  slot_mapping, num_tokens, num_blocks, num_kv_heads,
                                                  head_dim, dtype, (hipStream_t)stream);

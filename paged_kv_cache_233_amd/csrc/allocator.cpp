@@ -26,7 +26,7 @@
 #include <unordered_set>
 #include <vector>
 
-#include "internal.h"
+#include "host.h"
 
 namespace {
 
@@ -227,6 +227,29 @@ int pkv_allocator_set_free_order(pkv_allocator* a, const int32_t* order, int32_t
   a->clear_cache();
   a->reset_queue(order, n);
   return PKV_OK;
+}
+
+int pkv_allocator_shuffle_free_list(pkv_allocator* a, uint64_t seed) {
+  pkv::clear_error();
+  if (int e = check_handle(a)) return e;
+  // Ids 1..nb-1 in ascending order, permuted by the Fisher-Yates shuffle in
+  // Durstenfeld's form (for i = n-1 down to 1, swap entry i with entry
+  // draw % (i+1)); the draws come from SplitMix64 (Steele, Lea and Flood,
+  // "Fast splittable pseudorandom number generators", OOPSLA 2014): the
+  // state advances by 0x9E3779B97F4A7C15 and each draw is that state mixed
+  // by two xor-shift-multiply rounds and a final xor-shift.
+  std::vector<int32_t> order(a->nb - 1);
+  for (int32_t i = 0; i < a->nb - 1; ++i) order[i] = i + 1;
+  uint64_t state = seed;
+  for (int32_t i = a->nb - 2; i >= 1; --i) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    std::swap(order[i], order[(size_t)(z % (uint64_t)(i + 1))]);
+  }
+  return pkv_allocator_set_free_order(a, order.data(), a->nb - 1);
 }
 
 int pkv_seq_add(pkv_allocator* a, int64_t seq_id) {

@@ -1,30 +1,17 @@
-// Internal declarations shared by the host-side translation units of libpkv.
+// Internal declarations of the translation units of libpkv that launch
+// kernels (the host-only ones include host.h alone).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
-#include <cstdarg>
-#include <cstdint>
 #include <string>
 
-#include "pkv.h"
+#include "host.h"
 
 namespace pkv {
 
-// Records a message for pkv_last_error() and returns `code`.
-int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-// Clears the per-thread message.
-void clear_error();
 // Maps a HIP error from a launch to PKV_ERR_HIP with a message.
 int hip_fail(hipError_t e, const char* what);
-
-constexpr int kBlock = PKV_BLOCK_SIZE;
-
-// SHA-256 of n bytes; the seed hash of a first block; the chained content
-// hash of one full block (parent may be NULL for the first block).
-void sha256(const void* data, size_t n, uint8_t out[32]);
-const uint8_t* none_hash();
-void block_hash(const uint8_t* parent, const int32_t* tokens, uint64_t extra, uint8_t out[32]);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments were validated by

@@ -24,7 +24,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "internal.h"
+#include "host.h"
 
 namespace {
 

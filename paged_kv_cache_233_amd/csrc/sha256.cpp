@@ -17,7 +17,7 @@
 // roots.
 #include <cstring>
 
-#include "internal.h"
+#include "host.h"
 
 namespace pkv {
 namespace {

@@ -8,3 +8,5 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "full_library: calls entry points that only libpkv.so has (not the "
+                                       "host-only sanitizer build)")

@@ -68,6 +68,38 @@ def test_reshape_and_cache_strided_source():
     assert to_numpy_storage(vc).tobytes() == ov.tobytes()
 
 
+def test_reshape_and_cache_debug_mode_refuses_bad_slot_mappings():
+    """With the debug checks on, a slot mapping with a repeated slot, a slot
+    in the null block or one outside the pool is refused before any launch
+    (the pools keep their canaries); a good one is scattered as usual."""
+    _announce("reshape_and_cache debug checks")
+    nb, hkv, d, t = 9, 2, 64, 6
+    k_new = torch.randn((t, hkv, d), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    v_new = torch.randn((t, hkv, d), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    kc = torch.full((nb, hkv, 16, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    pkv.set_debug_checks(True)
+    try:
+        for bad in ([20, 21, 22, 20, -1, 30], [20, 21, 5, 23, -1, 30], [20, 21, 22, 23, -1, 144]):
+            with pytest.raises(pkv.Error) as e:
+                pkv.reshape_and_cache(kc, vc, k_new.cuda(), v_new.cuda(),
+                                      torch.tensor(bad, dtype=torch.int64, device="cuda"))
+            assert e.value.code == pkv.ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert torch.isnan(kc.float()).all() and torch.isnan(vc.float()).all()
+        good = np.array([20, 21, 22, 23, -1, 30], dtype=np.int64)
+        pkv.reshape_and_cache(kc, vc, k_new.cuda(), v_new.cuda(), torch.from_numpy(good).cuda())
+        torch.cuda.synchronize()
+    finally:
+        pkv.set_debug_checks(False)
+    ok = paged.new_pool(nb, hkv, d, "bf16")
+    ov = paged.new_pool(nb, hkv, d, "bf16")
+    paged.scatter(ok, to_numpy_storage(k_new), good)
+    paged.scatter(ov, to_numpy_storage(v_new), good)
+    assert to_numpy_storage(kc).tobytes() == ok.tobytes()
+    assert to_numpy_storage(vc).tobytes() == ov.tobytes()
+
+
 def test_copy_blocks_bit_exact():
     _announce("copy_blocks")
     nb, hkv, d = 12, 8, 128
@@ -244,7 +276,7 @@ def test_decode_workspace_too_small():
 
 
 # ------------------------------------------------------ full-size workloads
-FULL_SAMPLES = {"llama": [0, 5, 17, 33, 63], "long": [3], "shared": [0, 1, 64, 127],
+FULL_SAMPLES = {"llama": [0, 5, 17, 33, 63], "long": list(range(8)), "shared": [0, 1, 64, 127],
                 "mixed": [0, 7, 15]}
 
 

@@ -1,5 +1,6 @@
 """A whole decode step (index staging, reshape_and_cache, split-KV and merge
 kernels) captured as one HIP graph and replayed: every replay equals the
+CPU oracle (pools bit for bit, outputs within the bf16 tolerance) and the
 same step run eagerly, bit for bit. The entry points never synchronise with
 the host or allocate, which is what capture needs ("(2) vLLM Internals: From
 PagedAttention to Removing PagedAttention", section 4.2, on capturing a whole
@@ -10,7 +11,8 @@ import torch
 
 import paged_kv_cache_233_amd as pkv
 import workloads
-from tests.pipeline import run_native
+from oracle import paged
+from tests.pipeline import assert_close, run_native, run_oracle, to_numpy_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +22,10 @@ def test_decode_step_graph_replays_equal_eager():
     w = workloads.custom("gr", 60, [700, 1500, 33, 2048], num_q_heads=32, num_kv_heads=8,
                          head_dim=128, dtype="bf16")
     nat = run_native(w, prefill=False)
+    ora = run_oracle(w, prefill=False)
+    # the oracle's pools follow every replay's scatter on the CPU
+    ok, ov = ora["k_cache"].copy(), ora["v_cache"].copy()
+    assert to_numpy_storage(nat["k_cache"]).tobytes() == ok.tobytes()
     dec = w.decode_seqs
     S = len(dec)
     table, lens = nat["decode_table"], nat["decode_lens"]
@@ -73,6 +79,13 @@ def test_decode_step_graph_replays_equal_eager():
         torch.cuda.synchronize()
         step(kc_ref, vc_ref, ref)          # the same step, eagerly
         torch.cuda.synchronize()
+        # the oracle: the same scatter, then decode by definition
+        paged.scatter(ok, to_numpy_storage(k_new), slots)
+        paged.scatter(ov, to_numpy_storage(v_new), slots)
+        assert to_numpy_storage(kc).tobytes() == ok.tobytes(), rep
+        assert to_numpy_storage(vc).tobytes() == ov.tobytes(), rep
+        want = paged.decode(to_numpy_storage(q), ok, ov, ora["decode_table"], ln, w.scale)
+        assert_close(out, want, "bf16", "graph replay %d" % rep)
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
         assert torch.equal(kc.view(torch.int16), kc_ref.view(torch.int16)), rep
         assert torch.equal(vc.view(torch.int16), vc_ref.view(torch.int16)), rep

@@ -56,16 +56,19 @@ def test_shared_prefix_empty_suffix_and_fallbacks():
     w = workloads.custom("spe", 71, [48 + x for x in SUFFIX], shared_prefix=48,
                          num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16")
     nat = run_native(w, prefill=False)
+    ora = run_oracle(w, prefill=False)
     q, table, lens = _inputs(w, nat)
-    lens2 = nat["decode_lens"].copy()
+    # the reference: the oracle's own pools, table and lengths, and the
+    # workload's own queries
+    qs = np.concatenate([to_numpy_storage(w.seq_q(s)) for s in w.decode_seqs])
+    lens2 = ora["decode_lens"].copy()
     lens2[2] = 48
     lens2[5] = 48
     out = torch.empty_like(q)
     pkv.decode_shared_prefix(out, q, nat["k_cache"], nat["v_cache"], table,
                              torch.from_numpy(lens2).cuda(), 3, w.scale)
     torch.cuda.synchronize()
-    ref = paged.decode(to_numpy_storage(q.cpu()), to_numpy_storage(nat["k_cache"].cpu()),
-                       to_numpy_storage(nat["v_cache"].cpu()), nat["decode_table"], lens2, w.scale)
+    ref = paged.decode(qs, ora["k_cache"], ora["v_cache"], ora["decode_table"], lens2, w.scale)
     assert_close(out, ref, "bf16", "empty suffix")
     # prefix_blocks 0: the ordinary decode
     ws = pkv.decode_shared_prefix_workspace_size(len(w.decode_seqs), 32, 8, 128, 0)
@@ -74,6 +77,7 @@ def test_shared_prefix_empty_suffix_and_fallbacks():
                              torch.empty(ws, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(out0.view(torch.int16), nat["decode"].view(torch.int16))
+    assert_close(out0, ora["decode"], "bf16", "prefix_blocks 0")
     # fp32: the ordinary decode
     wf = workloads.custom("spf", 72, [48 + x for x in SUFFIX], shared_prefix=48,
                           num_q_heads=8, num_kv_heads=2, head_dim=64, dtype="f32")
@@ -83,6 +87,7 @@ def test_shared_prefix_empty_suffix_and_fallbacks():
     pkv.decode_shared_prefix(outf, qf, natf["k_cache"], natf["v_cache"], tf, lf, 3, wf.scale)
     torch.cuda.synchronize()
     assert torch.equal(outf, natf["decode"])
+    assert_close(outf, run_oracle(wf, prefill=False)["decode"], "f32", "fp32 fallback")
 
 
 def test_shared_prefix_workspace_too_small():

@@ -35,6 +35,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= set(pkv._SIGNATURES)
 
 
+@pytest.mark.full_library
 def test_decode_waves_setter_checks_its_argument():
     """Host-only: out-of-range values are refused, 0 restores the default."""
     with pytest.raises(pkv.Error) as e:
@@ -215,6 +216,7 @@ def _raw(name, *args):
     return getattr(pkv.library(), name)(*args)
 
 
+@pytest.mark.full_library
 def test_device_entry_points_reject_bad_arguments():
     """Checks made on the host before anything is launched."""
     # head_dim 96 is not built
@@ -299,3 +301,57 @@ def test_product_code_does_not_use_the_oracle():
                 text = open(os.path.join(root, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "tests." not in text, f
+
+
+# ------------------------------------------------- seeded placement, slot check
+def test_splitmix64_reference_outputs():
+    """The model's generator against the first outputs of the published
+    SplitMix64 reference implementation for seed 1234567."""
+    assert amodel.splitmix64(1234567, 5) == [6457827717110365317, 3203168211198807973,
+                                             9817491932198370423, 4593380528125082431,
+                                             16408922859458223821]
+
+
+@pytest.mark.parametrize("nb,seed", [(2, 0), (3, 1), (40, 7), (1000, 2 ** 64 - 1), (12346, 1)])
+def test_shuffle_free_list_matches_model(nb, seed):
+    """C++ shuffle == model shuffle (two implementations of one definition);
+    the result is a permutation of 1..NB-1 that the allocator hands out in
+    order."""
+    c = pkv.Allocator(nb)
+    c.shuffle_free_list(seed)
+    m = amodel.AllocatorModel(nb)
+    m.shuffle_free_list(seed)
+    assert sorted(m.free) == list(range(1, nb))
+    c.add(1)
+    m.add(1)
+    s1, _ = c.append(1, 16 * (nb - 1))
+    s2, _ = m.append(1, 16 * (nb - 1))
+    assert list(s1) == list(s2)
+    assert [x // 16 for x in s2[::16]] == list(m.blocks[1])
+
+
+def test_shuffle_depends_on_the_seed_and_needs_an_empty_pool():
+    orders = []
+    for seed in (1, 2, 1):
+        m = amodel.AllocatorModel(64)
+        m.shuffle_free_list(seed)
+        orders.append(list(m.free))
+    assert orders[0] == orders[2] and orders[0] != orders[1]
+    c = pkv.Allocator(8)
+    c.add(1)
+    c.append(1, 3)
+    with pytest.raises(pkv.Error) as e:
+        c.shuffle_free_list(5)
+    assert e.value.code == pkv.ERR_INVALID_ARG
+
+
+def test_slot_mapping_check():
+    """One slot per token, never the null block, inside the pool; padding
+    (negative) passes."""
+    nb = 10
+    pkv.check_slot_mapping(np.array([16, 17, -1, -1, 159, 40], np.int64), nb)
+    pkv.check_slot_mapping(np.array([], np.int64), nb)
+    for bad, what in (([16, 40, 16], "repeats"), ([3, 20], "null block"), ([20, 160], "outside")):
+        with pytest.raises(pkv.Error) as e:
+            pkv.check_slot_mapping(np.array(bad, np.int64), nb)
+        assert e.value.code == pkv.ERR_INVALID_ARG and what in e.value.message

@@ -109,6 +109,89 @@ def test_scatter_roundtrip():
     check_scatter_roundtrip()
 
 
+def check_copy_blocks_direction():
+    """Copy-on-write gives the writer a private copy of the shared block
+    ("(2) vLLM Internals ...", 1.2 "Three Direct Wins", item 2): after a
+    (src, dst) pair, dst holds src's former bytes and src is unchanged. Every
+    block starts with distinct finite contents, so a copy run the wrong way
+    (or a swap) shows. Pairs apply in order: a chain (a, b), (b, c) carries
+    a's bytes on to c."""
+    rng = np.random.default_rng(15)
+    nb, hkv, d = 9, 2, 8
+    for storage in ("f32", "bf16"):
+        pool = _rand_pool(rng, nb, hkv, d, storage)
+        before = pool.copy()
+        assert all(not np.array_equal(before[i], before[j]) for i in range(nb) for j in range(i))
+        paged.copy_blocks(pool, [(1, 5), (2, 7), (5, 8)])
+        assert pool[5].tobytes() == before[1].tobytes()
+        assert pool[7].tobytes() == before[2].tobytes()
+        assert pool[8].tobytes() == before[1].tobytes()
+        for b in (0, 1, 2, 3, 4, 6):
+            assert pool[b].tobytes() == before[b].tobytes()
+        pool2 = before.copy()
+        paged.copy_blocks(pool2, np.array([[3, 4]], dtype=np.int64))
+        assert pool2[4].tobytes() == before[3].tobytes() and pool2[3].tobytes() == before[3].tobytes()
+
+
+def test_copy_blocks_direction():
+    check_copy_blocks_direction()
+
+
+def check_cow_fork_append_stream():
+    """End to end on the CPU: a parent with a partially filled last block is
+    forked, both then append into that shared block. The allocator model
+    emits a copy-on-write pair for the first writer, the oracle applies it
+    with copy_blocks before scattering the step's tokens ("vLLM: what
+    PagedAttention turned into", "What a block hash actually is": a shared
+    tail is redirected into a private copy-on-write block), and decode over
+    the paged pools must equal unpaged attention over each sequence's own
+    tokens (attend_sequence). Fresh blocks hold NaN, so a copy that is
+    missing or runs the wrong way poisons an output."""
+    rng = np.random.default_rng(16)
+    hq, hkv, d, nb = 4, 2, 8, 24
+    a = amodel.AllocatorModel(nb)
+    kp = paged.new_pool(nb, hkv, d, "f32")
+    vp = paged.new_pool(nb, hkv, d, "f32")
+    toks = {}
+
+    def put(sid, n):
+        slots, pairs = a.append(sid, n)
+        paged.copy_blocks(kp, pairs)
+        paged.copy_blocks(vp, pairs)
+        k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        paged.scatter(kp, k, slots)
+        paged.scatter(vp, v, slots)
+        pk, pv = toks.get(sid, (np.zeros((0, hkv, d), np.float32),) * 2)
+        toks[sid] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
+        return pairs
+
+    a.add(1)
+    assert put(1, 21) == []                    # blocks 1 (full) and 2 (5 tokens)
+    a.fork(1, 2)
+    toks[2] = (toks[1][0].copy(), toks[1][1].copy())
+    a.fork(1, 3)
+    toks[3] = (toks[1][0].copy(), toks[1][1].copy())
+    pairs = put(2, 3)                          # the child writes into the shared tail first
+    assert len(pairs) == 1 and pairs[0][0] == a.blocks[1][1] and pairs[0][1] == a.blocks[2][1]
+    assert put(3, 14) != []                    # a second child: its own private copy
+    assert put(1, 2) == []                     # the parent is the last holder: in place
+    assert put(2, 30) == []
+    sids = [1, 2, 3]
+    table, lens = a.block_table(sids, 4)
+    q = rng.standard_normal((3, hq, d)).astype(np.float32)
+    out = paged.decode(q, kp, vp, table, lens, 0.4)
+    for i, sid in enumerate(sids):
+        k, v = toks[sid]
+        ref = paged.attend_sequence(q[i:i + 1], k, v, [k.shape[0] - 1], 0.4)
+        assert np.isfinite(out[i]).all()
+        assert np.max(np.abs(out[i] - ref[0])) < 1e-12
+
+
+def test_cow_fork_append_stream():
+    check_cow_fork_append_stream()
+
+
 def test_bf16_widening_exact():
     # 1.0, -2.0, 0.5, max finite, smallest normal, a subnormal, 1 + 2^-7
     bits = np.array([0x3F80, 0xC000, 0x3F00, 0x7F7F, 0x0080, 0x0001, 0x3F81], dtype=np.uint16)
@@ -521,7 +604,8 @@ def _raises(check):
     return False
 
 
-ALL_CHECKS = [check_block_table_example, check_scatter_roundtrip, check_two_token_closed_form,
+ALL_CHECKS = [check_block_table_example, check_scatter_roundtrip, check_copy_blocks_direction,
+              check_cow_fork_append_stream, check_two_token_closed_form,
               check_single_token_is_value, check_uniform_scores_give_mean, check_dominant_key,
               check_gqa_mapping, check_placement_and_sharing_invariance, check_causal_mask,
               check_prefill_matches_decode_and_splits, check_allocator_policy,
@@ -598,6 +682,11 @@ def _mut_sequence_window_short(q, k, v, positions, scale):
 _orig_sequence = paged.attend_sequence
 
 
+def _mut_copy_reversed(pool, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        pool[src] = pool[dst]
+
+
 class _FifoModel(amodel.AllocatorModel):
     def free_seq(self, sid):
         released = []
@@ -642,6 +731,7 @@ MUTANTS = {
     "kv head h % Hkv": (paged, "decode", _mut_gqa_modulo),
     "causal window one short": (paged, "prefill_chunk", _mut_causal_off_by_one),
     "sequence window one short": (paged, "attend_sequence", _mut_sequence_window_short),
+    "copy-on-write copy reversed": (paged, "copy_blocks", _mut_copy_reversed),
     "FIFO free list": (amodel, "AllocatorModel", _FifoModel),
     "head-first free": (amodel, "AllocatorModel", _HeadFirstModel),
     "no copy-on-write": (amodel, "AllocatorModel", _NoCowModel),

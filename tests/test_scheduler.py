@@ -195,8 +195,9 @@ def test_request_preempts_itself(impl):
 
 @pytest.mark.parametrize("impl", IMPLS)
 def test_preempted_request_hits_its_own_prefix(impl):
-    """Freed blocks keep their hashes: a preempted request that comes back
-    before its blocks are reused attaches them and recomputes only the rest."""
+    """A preempted request whose freed, still-hashed blocks have not been
+    handed out again reattaches them on readmission and recomputes only the
+    tokens after them."""
     s = Both(impl, 7, 128, caching=True)           # 6 usable blocks
     s.add(1, list(range(40)), 10)                  # 3 blocks; its 49th token needs a 4th
     s.add(2, list(range(200, 232)), 30)            # 2 blocks, a 3rd from its 33rd token
