@@ -414,6 +414,29 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
                                      float scale, int32_t dtype, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Size of the scratch array each GPU holds for pkv_paged_attention_decode_noalloc. */
+#define PKV_DECODE_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * of pkv_paged_attention_decode, same arguments and same kernels, minus the
+ * workspace. Its bookkeeping and partial states live in a file-scope device
+ * array of PKV_DECODE_SCRATCH_BYTES (16 MiB) that every GPU the library runs
+ * on holds until the process ends; the call allocates nothing (the first call
+ * on a device looks the array's device address up once). Sizes whose decode
+ * workspace (pkv_decode_workspace_size) exceeds the array are refused with
+ * PKV_ERR_WORKSPACE: about 4 MB at 4 query heads per KV head and head_dim 128
+ * with the default 3 waves per CU, 13 MB at 16. All calls on one GPU share
+ * the array, which keeps the last call's contents (the decode needs no
+ * initialisation of it): calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. */
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_table,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       float scale, int32_t dtype, void* stream);
+
 /* Workspace bytes pkv_paged_attention_decode_shared_prefix needs for these
  * sizes on the current device. */
 int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,

@@ -109,6 +109,9 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
                                    ctypes.c_int),
+    "pkv_paged_attention_decode_noalloc": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p],
+                                           ctypes.c_int),
     "pkv_paged_attention_decode_split": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p,
                                           _c_sz, _c_p], ctypes.c_int),
@@ -646,6 +649,27 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
         (out, q, k_cache, v_cache, block_table, context_lens, workspace), prepare)
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_table, context_lens, scale: float,
+                   stream=None, prepare=False):
+    """Paged decode attention without a workspace: the library's per-GPU
+    scratch array (PKV_DECODE_SCRATCH_BYTES) holds the partial states. Calls
+    that overlap on one GPU race."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
+        raise Error(ERR_INVALID_ARG, "q/out must be [S, Hq, %d]" % d)
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    s, hq = int(q.shape[0]), int(q.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != s or context_lens.numel() != s:
+        raise Error(ERR_INVALID_ARG, "block_table must be [S, maxB] and context_lens [S]")
+    return _run(library().pkv_paged_attention_decode_noalloc, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32),
+        s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q), _stream(stream)),
+        (out, q, k_cache, v_cache, block_table, context_lens), prepare)
 
 
 def decode_shared_prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,

@@ -209,6 +209,32 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
                       workspace, workspace_bytes, stream, 2);
 }
 
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_table,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       float scale, int32_t dtype, void* stream) {
+  pkv::clear_error();
+  if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
+  if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_seqs == 0) return PKV_OK;
+  if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  if (need > (size_t)PKV_DECODE_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "the no-alloc decode's scratch holds %zu bytes; these sizes need %zu (use "
+                "pkv_paged_attention_decode with a workspace)",
+                (size_t)PKV_DECODE_SCRATCH_BYTES, need);
+  void* scratch = nullptr;
+  hipError_t err = pkv::decode_scratch(&scratch);
+  if (err != hipSuccess) return pkv::hip_fail(err, "no-alloc decode scratch lookup");
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      scratch, (size_t)PKV_DECODE_SCRATCH_BYTES, stream, 3);
+}
+
 // Workspace of the shared-prefix decode: the decode workspace, then the
 // prefix states (parts x num_seqs x num_q_heads x (head_dim + 4) floats),
 // which the decode folds at each sequence's first piece.

@@ -29,9 +29,13 @@
 // carry zero queries and are never stored.
 #include <atomic>
 #include <cstdlib>
+#include <mutex>
 
 #include "internal.h"
 #include "tile_attn.h"
+
+// (the scratch array of the no-alloc decode; see decode_scratch below)
+static __device__ __align__(256) char scratch[PKV_DECODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -662,9 +666,38 @@ hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
   return hipSuccess;
 }
 
+
+// Scratch of the no-alloc decode (pkv_paged_attention_decode_noalloc): the
+// same bookkeeping and partial states the decode keeps in a caller's
+// workspace, in a file-scope device array instead. Every GPU the library runs
+// on holds its own copy for the life of the process. In host code `scratch`
+// names a host-side stand-in, not device memory: the device address of each
+// GPU's copy comes from hipGetSymbolAddress and is the only one ever passed
+// to a kernel.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address per device (nullptr: not looked up yet)
+
 }  // namespace
 
 namespace pkv {
+
+hipError_t decode_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    // with this device current: its own copy of the array
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (uintptr_t)ptr % 256 != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 void decode_set_waves_per_cu(int per_cu) {
   g_waves_per_cu.store(per_cu, std::memory_order_relaxed);

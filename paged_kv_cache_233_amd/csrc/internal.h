@@ -57,6 +57,9 @@ int decode_num_waves();
 void decode_set_waves_per_cu(int per_cu);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim);
+// Device address of the current device's copy of the no-alloc decode's
+// scratch array (PKV_DECODE_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t decode_scratch(void** out);
 // phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.
 hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream);
 // Decode over each sequence's blocks from `skip_blocks` on, starting every
