@@ -83,6 +83,8 @@ def parse():
                     help="only run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--shared-probe", action="store_true",
                     help="only run the shared-prefix leg and print its JSON (for profiling it alone)")
+    ap.add_argument("--prefill-probe", action="store_true",
+                    help="only run the chunked-prefill leg and print its JSON (for profiling it alone)")
     return ap.parse_args()
 
 
@@ -475,6 +477,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.shared_probe:
         print(json.dumps({"shared_prefix": shared_leg(args, dev)}), flush=True)
+        return
+    if args.prefill_probe:
+        print(json.dumps({"prefill": prefill_leg(args, dev)}), flush=True)
         return
     w = workloads.named(args.config)
     hip = HipEvents()

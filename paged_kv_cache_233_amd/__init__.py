@@ -133,6 +133,9 @@ def library() -> ctypes.CDLL:
         if _lib is None:
             host_only = os.environ.get("PKV_HOST_SANITIZED") == "1"
             path = HOST_SANITIZED_LIB_PATH if host_only else LIB_PATH
+            # another build of the same library (same entry points), e.g. an
+            # instrumented one
+            path = os.environ.get("PKV_LIBRARY", path)
             if not os.path.exists(path):
                 from . import build as _build
                 if host_only:
