@@ -214,34 +214,69 @@ __device__ __forceinline__ void zero_rows(const DecodeParams& p, int32_t s) {
     *reinterpret_cast<uint4*>(row + e * Shape<DT, D>::kElem) = uint4{0u, 0u, 0u, 0u};
 }
 
-// Partial states whose loads the merge issues together (8 or 16 were
-// slower on sequences split over a dozen waves: 11.2 and 12.4 us against
-// 9.4 us for the merge launch).
+// Partial states whose loads one merge thread issues together.
 constexpr int kMergeBatch = 4;
+// Waves of the merge workgroup: each folds a contiguous quarter of a split
+// sequence's partial states, then the first folds the four results in order.
+constexpr int kMergeWaves = 4;
+
+// Running fold of partial softmax states for 8 consecutive output values of
+// one query head.
+struct Fold {
+  float mx, den;
+  float num[8];
+  __device__ __forceinline__ void reset() {
+    mx = -INFINITY;
+    den = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) num[i] = 0.f;
+  }
+  // Add a state (max m, sum l, unnormalised values o) to the fold: the
+  // online-softmax rescale to the larger of the two maxima.
+  __device__ __forceinline__ void add(float m, float l, const float (&o)[8]) {
+    const float m_new = fmaxf(mx, m);
+    const float so = __builtin_amdgcn_exp2f(mx - m_new);
+    const float sk = __builtin_amdgcn_exp2f(m - m_new);
+    den = den * so + l * sk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) num[i] = num[i] * so + o[i] * sk;
+    mx = m_new;
+  }
+};
 
 // Fold the partial states of sequence s, KV head g (flat tiles first..last)
-// in wave order and write the normalised output. Each lane owns 8
-// consecutive output values of one query head; the states are read
-// kMergeBatch at a time with their loads issued together. A wave whose
-// range starts before the sequence holds its state in its second slot,
-// every other wave in its first.
+// and write the normalised output. The owners of the sequence's tiles are
+// waves w0..w1 (in token order); merge wave k folds the contiguous quarter
+// [w0 + k*n/4, w0 + (k+1)*n/4) of them in order, each lane owning 8
+// consecutive output values of one query head and issuing the loads of
+// kMergeBatch states together; merge wave 0 then folds the four results in
+// order through LDS. The order is fixed, so the result is deterministic. A
+// wave whose range starts before the sequence holds its state in its second
+// slot, every other wave in its first.
 template <int DT, int D>
 __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t first,
                                int32_t last, const WaveRanges& R) {
-  const int lane = threadIdx.x;
+  __shared__ float xs[kMergeWaves - 1][10][64];
+  const int lane = threadIdx.x & 63;
+  const int mw = threadIdx.x >> 6;
   const int32_t G = p.group;
   const int64_t out_row = ((int64_t)s * p.num_q_heads + (int64_t)g * G) * D;
   const int32_t w0 = R.owner(first), w1 = R.owner(last);
+  const int32_t nw = w1 - w0 + 1;
+  const int32_t wa = w0 + (mw * nw) / kMergeWaves;
+  const int32_t wb = w0 + ((mw + 1) * nw) / kMergeWaves;
   const int32_t stride = G * (D + 4);
-  for (int32_t e = 8 * lane; e < G * D; e += 512) {
-    const int32_t h = e / D;
-    float mx = -INFINITY, den = 0.f;
-    float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int32_t wv = w0;
-    while (wv <= w1) {
+  for (int32_t e0 = 0; e0 < G * D; e0 += 512) {
+    const int32_t e = e0 + 8 * lane;
+    const bool act = e < G * D;
+    const int32_t h = act ? e / D : 0;
+    Fold f;
+    f.reset();
+    int32_t wv = wa;
+    while (act && wv < wb) {
       int32_t slot[kMergeBatch];
       int cnt = 0;
-      for (; wv <= w1 && cnt < kMergeBatch; ++wv) {
+      for (; wv < wb && cnt < kMergeBatch; ++wv) {
         if (R.empty(wv)) continue;
         slot[cnt++] = 2 * wv + (R.begin(wv) < first ? 1 : 0);
       }
@@ -260,32 +295,44 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
         if (k < cnt) {
-          const float m_new = fmaxf(mx, mk[k]);
-          const float so = __builtin_amdgcn_exp2f(mx - m_new);
-          const float sk = __builtin_amdgcn_exp2f(mk[k] - m_new);
-          den = den * so + lk[k] * sk;
           const float ov[8] = {o0[k].x, o0[k].y, o0[k].z, o0[k].w, o1[k].x, o1[k].y, o1[k].z, o1[k].w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) num[i] = num[i] * so + ov[i] * sk;
-          mx = m_new;
+          f.add(mk[k], lk[k], ov);
         }
       }
     }
-    const float inv = 1.0f / den;
-    if constexpr (DT == PKV_BF16) {
-      uint32_t wd[4];
+    if (mw > 0) {
+      xs[mw - 1][0][lane] = f.mx;
+      xs[mw - 1][1][lane] = f.den;
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        bf16x2 v = {(__bf16)(num[i] * inv), (__bf16)(num[i + 1] * inv)};
-        wd[i / 2] = __builtin_bit_cast(uint32_t, v);
-      }
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + out_row + e) =
-          uint4{wd[0], wd[1], wd[2], wd[3]};
-    } else {
-      float* o = reinterpret_cast<float*>(p.out) + out_row + e;
-      *reinterpret_cast<float4*>(o) = float4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
-      *reinterpret_cast<float4*>(o + 4) = float4{num[4] * inv, num[5] * inv, num[6] * inv, num[7] * inv};
+      for (int i = 0; i < 8; ++i) xs[mw - 1][2 + i][lane] = f.num[i];
     }
+    __syncthreads();
+    if (mw == 0 && act) {
+#pragma unroll
+      for (int k = 0; k < kMergeWaves - 1; ++k) {
+        float ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ov[i] = xs[k][2 + i][lane];
+        // (an empty quarter has max -inf and sum 0: weight 0)
+        if (xs[k][0][lane] != -INFINITY) f.add(xs[k][0][lane], xs[k][1][lane], ov);
+      }
+      const float inv = 1.0f / f.den;
+      if constexpr (DT == PKV_BF16) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          bf16x2 v = {(__bf16)(f.num[i] * inv), (__bf16)(f.num[i + 1] * inv)};
+          wd[i / 2] = __builtin_bit_cast(uint32_t, v);
+        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + out_row + e) =
+            uint4{wd[0], wd[1], wd[2], wd[3]};
+      } else {
+        float* o = reinterpret_cast<float*>(p.out) + out_row + e;
+        *reinterpret_cast<float4*>(o) = float4{f.num[0] * inv, f.num[1] * inv, f.num[2] * inv, f.num[3] * inv};
+        *reinterpret_cast<float4*>(o + 4) = float4{f.num[4] * inv, f.num[5] * inv, f.num[6] * inv, f.num[7] * inv};
+      }
+    }
+    __syncthreads();   // the LDS slots are reused by the next chunk of values
   }
 }
 
@@ -595,11 +642,11 @@ decode_split_kernel(DecodeParams p) {
 }
 
 // Merge the partial states of every sequence whose tiles were split across
-// waves. One wave per (sequence, KV head); sequences held by a single wave
+// waves. One workgroup per (sequence, KV head); sequences held by a single wave
 // (written directly) and empty sequences (zeroed by the split kernel) are
 // skipped.
 template <int DT, int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64 * kMergeWaves)
 decode_merge_kernel(DecodeParams p) {
   const int32_t s = blockIdx.x / p.num_kv_heads;
   const int32_t g = blockIdx.x - s * p.num_kv_heads;
@@ -659,7 +706,7 @@ hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (phases & 2) {
-    hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(prm.num_seqs * prm.num_kv_heads), dim3(64),
+    hipLaunchKernelGGL((decode_merge_kernel<DT, D>), dim3(prm.num_seqs * prm.num_kv_heads), dim3(64 * kMergeWaves),
                        0, stream, prm);
     return hipGetLastError();
   }
