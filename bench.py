@@ -322,16 +322,18 @@ def decode_setup(w, args, dev, legs):
     return c
 
 
-def resident_leg(c, args, hip):
+def resident_leg(c, args, hip, fused=True):
     """The headline measurement of one workload: the host allocator plans
     every step first (one token appended to each sequence; the slots,
     lengths and block table of step t written into slice t of one pinned
     buffer), one copy puts all slices in HBM, then every planned step
-    (warm-up, then timed) runs reshape_and_cache, the split kernel and the
-    merge kernel with its indices resident. The planned steps run twice with
-    the same plans (same slots written, same bytes read): once with HIP
-    events around every kernel (per-kernel times; the event records add gaps
-    between the kernels), once without (the wall time behind the value)."""
+    (warm-up, then timed) runs with its indices resident: the split kernel
+    with the new token's cache write folded in (decode_append) and the merge
+    kernel, or with ``fused`` False, reshape_and_cache, the plain split
+    kernel and the merge kernel. The planned steps run twice with the same
+    plans (same slots written, same bytes read): once with HIP events around
+    every kernel (per-kernel times; the event records add gaps between the
+    kernels), once without (the wall time behind the value)."""
     import numpy as np
     import torch
 
@@ -359,24 +361,34 @@ def resident_leg(c, args, hip):
         lens = x[S:].view(torch.int32)[:S]
         table = x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb)
         kc, vc = c.pools[t % len(c.pools)]
-        launch.append((
-            pkv.reshape_and_cache(kc, vc, c.k_new, c.v_new, slots, stream=sh, prepare=True),
-            pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="split",
-                       prepare=True),
-            pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="merge",
-                       prepare=True)))
+        if fused:
+            launch.append((
+                None,
+                pkv.decode_append(c.out, c.q, c.k_new, c.v_new, kc, vc, table, lens, w.scale, c.ws,
+                                  stream=sh, phase="split", prepare=True),
+                pkv.decode_append(c.out, c.q, c.k_new, c.v_new, kc, vc, table, lens, w.scale, c.ws,
+                                  stream=sh, phase="merge", prepare=True)))
+        else:
+            launch.append((
+                pkv.reshape_and_cache(kc, vc, c.k_new, c.v_new, slots, stream=sh, prepare=True),
+                pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="split",
+                           prepare=True),
+                pkv.decode(c.out, c.q, kc, vc, table, lens, w.scale, c.ws, stream=sh, phase="merge",
+                           prepare=True)))
 
     def run(events):
         def step(t):
             reshape, split, merge = launch[t]
             if not events:
-                reshape()
+                if reshape is not None:
+                    reshape()
                 split()
                 merge()
                 return
             e0, e1, e2, e3 = ev[t]
             hip.record(e0, sh)
-            reshape()
+            if reshape is not None:
+                reshape()
             hip.record(e1, sh)
             split()                       # decode = split-KV kernel, then merge kernel
             hip.record(e2, sh)
@@ -411,17 +423,22 @@ def resident_leg(c, args, hip):
     split_b2b_us = hip.elapsed_us(b0, b1) / len(timed)
     del plan_d
     kv_bytes = np.array([ctx_tokens[t] * c.kv_bytes_per_token for t in timed], dtype=np.float64)
+    # the split kernel's algorithmic bytes: the K/V it reads, plus with the
+    # fused write the new token's K/V read from its buffer and written once
+    split_bytes = kv_bytes + (2 * S * c.kv_bytes_per_token if fused else 0)
     r = {"ctx": c, "wall": wall, "ev_wall": ev_wall, "us": us, "kv_bytes": kv_bytes,
+         "split_bytes": split_bytes, "fused": fused,
          "alloc_us": alloc_us, "ms_per_step": wall / args.steps * 1e3,
          "split_b2b_us": split_b2b_us,
          "value": float(kv_bytes.sum() / wall / 1e9),
-         "achieved": float(kv_bytes.mean() / (split_b2b_us * 1e-6) / 1e9),
+         "achieved": float(split_bytes.mean() / (split_b2b_us * 1e-6) / 1e9),
          "achieved_op": float(kv_bytes.mean() / (us["decode"].mean() * 1e-6) / 1e9)}
-    log("%s: decode kernels mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
+    log("%s%s: decode kernels mean %.1f us (min %.1f, median %.1f) = split %.1f + merge %.1f; "
         "reshape_and_cache %.1f us; step %.1f us wall (%.1f with events; indices resident) = "
         "%.1f GB/s (%.1f%% of peak); split kernel %.1f us back to back = %.1f%%; "
         "allocator %.1f us per step on the host"
-        % (w.name, us["decode"].mean(), us["decode"].min(), np.median(us["decode"]),
+        % (w.name, " (fused append)" if fused else " (reshape_and_cache + decode)",
+           us["decode"].mean(), us["decode"].min(), np.median(us["decode"]),
            us["split"].mean(), us["merge"].mean(), us["reshape"].mean(), r["ms_per_step"] * 1e3,
            ev_wall / args.steps * 1e6, r["value"], 100 * r["value"] / HBM_PEAK_GBS,
            split_b2b_us, 100 * r["achieved"] / HBM_PEAK_GBS, alloc_us))
@@ -447,31 +464,52 @@ def summary(c, r, args):
         "ms_per_step": round(r["ms_per_step"], 4),
         "pct_of_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(S * args.steps / r["wall"], 1),
-        # one layer's kernels only (event times): reshape_and_cache + split + merge
-        "kernel_tokens_per_s": round(S / ((rc_us.mean() + dec_us.mean()) * 1e-6), 1),
+        "step_kernels": ("decode_split_kernel with the new token's cache write (decode_append) "
+                         "+ decode_merge_kernel" if r["fused"] else
+                         "reshape_and_cache_kernel + decode_split_kernel + decode_merge_kernel"),
+        # one layer's kernels only (event times)
+        "kernel_tokens_per_s": round(S / (((0 if r["fused"] else rc_us.mean()) + dec_us.mean())
+                                          * 1e-6), 1),
         "kernel_us": {"decode_mean": round(float(dec_us.mean()), 2),
                       "decode_median": round(float(np.median(dec_us)), 2),
                       "decode_split_kernel_mean": round(float(split_us.mean()), 2),
                       "decode_split_kernel_back_to_back": round(r["split_b2b_us"], 2),
                       "decode_merge_kernel_mean": round(float(merge_us.mean()), 2),
-                      "reshape_and_cache_mean": round(float(rc_us.mean()), 2),
+                      "reshape_and_cache_mean": None if r["fused"] else round(float(rc_us.mean()), 2),
                       "step_with_events": round(r["ev_wall"] / args.steps * 1e6, 2),
                       "allocator_host_us_per_step": round(r["alloc_us"], 2)},
         "roofline": {"bound": "hbm", "achieved": round(r["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(decode_traffic_file(w.name)),
-                     "kernel": "decode_split_kernel (dominant kernel of paged_attention_decode)",
+                     "traffic": load_traffic(decode_traffic_file(w.name, r["fused"])),
+                     "kernel": "decode_split_kernel (dominant kernel of the decode step%s)"
+                               % (", new token's cache write folded in" if r["fused"] else ""),
                      "duration": "mean launch duration of the timed steps' split launches run "
                                  "back to back between one pair of HIP events",
-                     "algorithmic_bytes_per_launch": int(kv_bytes.mean())},
+                     "algorithmic_bytes_per_launch": int(r["split_bytes"].mean())},
         "decode_op": {"kernels": "decode_split_kernel + decode_merge_kernel",
                       "achieved_gbs": round(r["achieved_op"], 2),
                       "frac_of_hbm_peak": round(r["achieved_op"] / HBM_PEAK_GBS, 4)},
     }
 
 
-def decode_traffic_file(name):
-    return os.path.join(ROOT, "profiles", "decode_%s_traffic.json" % name)
+def decode_traffic_file(name, fused=False):
+    return os.path.join(ROOT, "profiles", "decode_%s%s_traffic.json"
+                        % (name, "_append" if fused else ""))
+
+
+def unfused_summary(r, args):
+    """The same workload's step with the cache write in its own kernel
+    (reshape_and_cache, then the plain split and merge kernels)."""
+    us = r["us"]
+    return {"ms_per_step": round(r["ms_per_step"], 4), "value_gbs": round(r["value"], 2),
+            "pct_of_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+            "kernel_us": {"reshape_and_cache_mean": round(float(us["reshape"].mean()), 2),
+                          "decode_split_kernel_mean": round(float(us["split"].mean()), 2),
+                          "decode_split_kernel_back_to_back": round(r["split_b2b_us"], 2),
+                          "decode_merge_kernel_mean": round(float(us["merge"].mean()), 2)},
+            "split_kernel_frac_of_hbm_peak": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "what": "reshape_and_cache_kernel + decode_split_kernel + decode_merge_kernel, "
+                    "same plans and pools"}
 
 
 def main():
@@ -500,8 +538,9 @@ def main():
     w = workloads.named(args.config)
     hip = HipEvents()
     sh = torch.cuda.current_stream().cuda_stream
-    ctx = decode_setup(w, args, dev, legs=3)        # resident, staged and graph legs
-    head = resident_leg(ctx, args, hip)
+    ctx = decode_setup(w, args, dev, legs=4)        # resident (fused, unfused), staged, graph
+    head = resident_leg(ctx, args, hip, fused=True)
+    unfused = resident_leg(ctx, args, hip, fused=False)
     S, maxb, words, dt = ctx.S, ctx.maxb, ctx.words, w.torch_dtype
     alloc, pools, sids, ones = ctx.alloc, ctx.pools, ctx.sids, ctx.ones
     q, k_new, v_new, out, ws = ctx.q, ctx.k_new, ctx.v_new, ctx.out, ctx.ws
@@ -526,7 +565,6 @@ def main():
     mapped = args.stage == "mapped"
     stage_mode = args.stage
     stage = pinned if mapped else [torch.empty(words, dtype=torch.int64, device=dev)] * 2
-    d_slots = [x[:S] for x in stage]
     d_lens = [x[S:].view(torch.int32)[:S] for x in stage]
     d_table = [x[S:].view(torch.int32)[S:S + S * maxb].view(S, maxb) for x in stage]
     # Every call of the step is checked and marshalled once per (staging
@@ -544,12 +582,13 @@ def main():
     slaunch = {}
     for b in range(2):
         for pi, (kc, vc) in enumerate(pools):
+            # the headline's kernels: the split kernel with the new
+            # token's cache write folded in, then the merge kernel
             slaunch[b, pi] = (
-                pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots[b], stream=sh, prepare=True),
-                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
-                           phase="split", prepare=True),
-                pkv.decode(out, q, kc, vc, d_table[b], d_lens[b], w.scale, ws, stream=sh,
-                           phase="merge", prepare=True))
+                pkv.decode_append(out, q, k_new, v_new, kc, vc, d_table[b], d_lens[b], w.scale, ws,
+                                  stream=sh, phase="split", prepare=True),
+                pkv.decode_append(out, q, k_new, v_new, kc, vc, d_table[b], d_lens[b], w.scale, ws,
+                                  stream=sh, phase="merge", prepare=True))
     waited = [0.0]
     s_tokens = []
 
@@ -569,8 +608,7 @@ def main():
         elif stage_mode == "dma":
             stage[b].copy_(pinned[b], non_blocking=True)
             hip.record(released[b], sh)
-        reshape, split, merge = slaunch[b, t % len(pools)]
-        reshape()
+        split, merge = slaunch[b, t % len(pools)]
         split()
         merge()
         if mapped:
@@ -598,7 +636,7 @@ def main():
                   "host_us_per_step": round(host_us, 2),
                   "what": "PCIe-inclusive: the host allocator plans each step inside the timed "
                           "loop and the slots, lengths and block table cross from pinned host "
-                          "memory to the device every step (%s), then the same three kernels"
+                          "memory to the device every step (%s), then the same two kernels"
                           % stage_mode}
         log("staged step (indices from pinned host memory each step, %s): %.1f us wall, "
             "%.1f GB/s, host work %.1f us per step" % (stage_mode, s_wall / args.steps * 1e6,
@@ -620,9 +658,8 @@ def main():
                 else:
                     stage[gb].copy_(pinned[gb], non_blocking=True)
                 kc, vc = pools[gidx]
-                pkv.reshape_and_cache(kc, vc, k_new, v_new, d_slots[gb])
-                pkv.decode(out, q, kc, vc, d_table[gb], d_lens[gb], w.scale, ws, phase="split")
-                pkv.decode(out, q, kc, vc, d_table[gb], d_lens[gb], w.scale, ws, phase="merge")
+                pkv.decode_append(out, q, k_new, v_new, kc, vc, d_table[gb], d_lens[gb], w.scale,
+                                  ws)
             graphs.append(g)
         torch.cuda.synchronize()
         g_tokens = []
@@ -651,7 +688,7 @@ def main():
         graph = {"ms_per_step": round(g_wall / args.steps * 1e3, 4),
                  "value": round(g_bytes / g_wall / 1e9, 2), "unit": "GB/s", "steps": args.steps,
                  "what": "the staged step replayed as one HIP graph per step (index staging, "
-                         "reshape_and_cache, split and merge kernels captured once per pool "
+                         "split kernel with the cache write, merge kernel captured once per pool "
                          "copy); timed after the eager runs, contexts still growing"}
         log("graph replay: step %.1f us wall, %.1f GB/s" % (g_wall / args.steps * 1e6,
                                                             graph["value"]))
@@ -662,8 +699,10 @@ def main():
     side = {}
     for name in SIDE_DECODE:
         if name != args.config and not args.no_side:
-            c2 = decode_setup(workloads.named(name), args, dev, legs=1)
-            side[name] = summary(c2, resident_leg(c2, args, hip), args)
+            c2 = decode_setup(workloads.named(name), args, dev, legs=2)
+            side[name] = summary(c2, resident_leg(c2, args, hip, fused=True), args)
+            side[name]["unfused_step"] = unfused_summary(resident_leg(c2, args, hip, fused=False),
+                                                         args)
             del c2
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
@@ -694,6 +733,7 @@ def main():
         "data": "synthetic",
     }
     res.update(summary(head["ctx"], head, args))
+    res["unfused_step"] = unfused_summary(unfused, args)
     res.update({
         "staged_step": staged,
         "graph_step": graph,

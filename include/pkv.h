@@ -414,6 +414,49 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
                                      float scale, int32_t dtype, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* A decode step with the current token's cache write folded into the
+ * split-KV kernel: the token's key and value are appended to each sequence's
+ * paged KV and attended in the same pass ["My Understanding of vLLM and
+ * PagedAttention", "Step 3 -- Tokens Generated Sequentially" and "Step 4 --
+ * Attention Computation"; "(2) vLLM Internals ...", 4.1 "Why It Could Go"].
+ * For each sequence s with n_s = context_lens[s] >= 1 (after the clamp of
+ * pkv_paged_attention_decode), the key and value rows k_new[s], v_new[s]
+ * ([num_kv_heads][head_dim], tokens new_token_stride elements apart, as in
+ * pkv_reshape_and_cache) are written to position n_s - 1 of s, i.e. slot
+ * block_table[s][(n_s-1)/16]*16 + (n_s-1)%16, and the output is then exactly
+ * what pkv_paged_attention_decode gives on the updated cache: the same as
+ * pkv_reshape_and_cache with that slot per sequence followed by
+ * pkv_paged_attention_decode, bit for bit, with one kernel fewer. A block id
+ * outside [1, num_blocks) at that position is not written (the attention
+ * then reads block 0, as the decode does for such ids). The block holding
+ * position n_s - 1 must be read by no other sequence of the call (a block
+ * being appended to is private: pkv_seq_append reports the copy-on-write
+ * pairs to run through pkv_copy_blocks first); otherwise the other sequence
+ * may see the old or the new row. k_cache and v_cache are written. Same errors as
+ * pkv_paged_attention_decode, plus PKV_ERR_INVALID_ARG for NULL or
+ * misaligned k_new/v_new or a stride below num_kv_heads*head_dim. */
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new,
+                                      const void* v_new, int64_t new_token_stride, void* k_cache,
+                                      void* v_cache, const int32_t* block_table,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+/* Its first phase alone (the split-KV kernel with the append), for callers
+ * that time the phases; the second is pkv_paged_attention_decode_merge with
+ * the same workspace and shared arguments. */
+int pkv_paged_attention_decode_append_split(void* out, const void* q, const void* k_new,
+                                            const void* v_new, int64_t new_token_stride,
+                                            void* k_cache, void* v_cache,
+                                            const int32_t* block_table,
+                                            const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float scale, int32_t dtype,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
 /* Size of the scratch array each GPU holds for pkv_paged_attention_decode_noalloc. */
 #define PKV_DECODE_SCRATCH_BYTES (16 * 1024 * 1024)
 

@@ -109,6 +109,13 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
                                    ctypes.c_int),
+    "pkv_paged_attention_decode_append": ([_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f,
+                                           _c_i32, _c_p, _c_sz, _c_p], ctypes.c_int),
+    "pkv_paged_attention_decode_append_split": ([_c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p,
+                                                 _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_f, _c_i32, _c_p, _c_sz, _c_p],
+                                                ctypes.c_int),
     "pkv_paged_attention_decode_noalloc": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_f, _c_i32, _c_p],
                                            ctypes.c_int),
@@ -652,6 +659,42 @@ def decode(out, q, k_cache, v_cache, block_table, context_lens, scale: float, wo
         s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
         (out, q, k_cache, v_cache, block_table, context_lens, workspace), prepare)
+
+
+def decode_append(out, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, scale: float,
+                  workspace, stream=None, phase: str = "both", prepare=False):
+    """A decode step with the current token's cache write folded in: k_new/v_new
+    [S, Hkv, D] are written to position context_lens[s] - 1 of each sequence
+    (through its block table), then the decode runs on the updated pools.
+    ``phase`` "split" launches the split-KV kernel (with the write) only,
+    "merge" the merge kernel only (call both, in that order)."""
+    torch = _torch()
+    nb, hkv, d = _pool_shape(k_cache)
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise Error(ERR_INVALID_ARG, "k_cache and v_cache differ")
+    if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):
+        raise Error(ERR_INVALID_ARG, "q/out must be [S, Hq, %d]" % d)
+    s, hq = int(q.shape[0]), int(q.shape[1])
+    if tuple(k_new.shape) != (s, hkv, d) or tuple(v_new.shape) != (s, hkv, d):
+        raise Error(ERR_INVALID_ARG, "k_new/v_new must be [%d, %d, %d]" % (s, hkv, d))
+    if any(x.dtype != k_cache.dtype for x in (q, out, k_new, v_new)):
+        raise Error(ERR_INVALID_ARG, "dtype mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != s or context_lens.numel() != s:
+        raise Error(ERR_INVALID_ARG, "block_table must be [S, maxB] and context_lens [S]")
+    idx = (_idx(block_table, "block_table", torch.int32), _idx(context_lens, "context_lens", torch.int32))
+    ws = (_dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
+    if phase == "merge":
+        return _run(library().pkv_paged_attention_decode_merge, (
+            _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            *idx, s, nb, int(block_table.shape[1]), hq, hkv, d, float(scale), _dtype_code(q), *ws,
+            _stream(stream)), (out, q, k_cache, v_cache, block_table, context_lens, workspace), prepare)
+    fn = {"both": library().pkv_paged_attention_decode_append,
+          "split": library().pkv_paged_attention_decode_append_split}[phase]
+    return _run(fn, (
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), hkv * d,
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), *idx, s, nb, int(block_table.shape[1]),
+        hq, hkv, d, float(scale), _dtype_code(q), *ws, _stream(stream)),
+        (out, q, k_new, v_new, k_cache, v_cache, block_table, context_lens, workspace), prepare)
 
 
 def decode_noalloc(out, q, k_cache, v_cache, block_table, context_lens, scale: float,

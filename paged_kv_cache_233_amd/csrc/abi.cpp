@@ -142,11 +142,19 @@ int pkv_decode_set_waves_per_cu(int32_t per_cu) {
 
 namespace {
 
+// The current token's K/V for the append mode of the decode (nullptr: none).
+struct NewTokens {
+  const void* k_new;
+  const void* v_new;
+  int64_t stride;
+};
+
 int decode_entry(void* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_table, const int32_t* context_lens, int32_t num_seqs,
                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t num_q_heads,
                  int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
-                 void* workspace, size_t workspace_bytes, void* stream, int phases) {
+                 void* workspace, size_t workspace_bytes, void* stream, int phases,
+                 const NewTokens* append = nullptr) {
   pkv::clear_error();
   if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
@@ -155,7 +163,8 @@ int decode_entry(void* out, const void* q, const void* k_cache, const void* v_ca
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (!block_table && max_blocks_per_seq > 0))
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
-  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 1) > INT32_MAX)
+  // (the decode partitions blocks plus a few units per sequence in int32)
+  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 16) > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs*num_kv_heads*max_blocks_per_seq too large");
   if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache |
        (uintptr_t)workspace) % 16 != 0)
@@ -168,6 +177,19 @@ int decode_entry(void* out, const void* q, const void* k_cache, const void* v_ca
   pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                     max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                     workspace};
+  if (append != nullptr) {
+    if (!append->k_new || !append->v_new) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+    if (append->stride < (int64_t)num_kv_heads * head_dim)
+      return fail(PKV_ERR_INVALID_ARG, "new_token_stride %lld < num_kv_heads*head_dim",
+                  (long long)append->stride);
+    const int64_t elem = dtype == PKV_F32 ? 4 : 2;
+    if (((uintptr_t)append->k_new | (uintptr_t)append->v_new) % 16 != 0 ||
+        (append->stride * elem) % 16 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "new K/V and the token stride must be 16-byte aligned");
+    a.k_new = append->k_new;
+    a.v_new = append->v_new;
+    a.new_token_stride = append->stride;
+  }
   hipError_t err = pkv::launch_decode(a, phases, (hipStream_t)stream);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
 }
@@ -207,6 +229,36 @@ int pkv_paged_attention_decode_merge(void* out, const void* q, const void* k_cac
   return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                       max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                       workspace, workspace_bytes, stream, 2);
+}
+
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new,
+                                      const void* v_new, int64_t new_token_stride, void* k_cache,
+                                      void* v_cache, const int32_t* block_table,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const NewTokens nt{k_new, v_new, new_token_stride};
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      workspace, workspace_bytes, stream, 3, &nt);
+}
+
+int pkv_paged_attention_decode_append_split(void* out, const void* q, const void* k_new,
+                                            const void* v_new, int64_t new_token_stride,
+                                            void* k_cache, void* v_cache,
+                                            const int32_t* block_table,
+                                            const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t num_blocks, int32_t max_blocks_per_seq,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float scale, int32_t dtype,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  const NewTokens nt{k_new, v_new, new_token_stride};
+  return decode_entry(out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
+                      max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                      workspace, workspace_bytes, stream, 1, &nt);
 }
 
 int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
@@ -283,7 +335,8 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !block_table)
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
-  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 1) > INT32_MAX)
+  // (the decode partitions blocks plus a few units per sequence in int32)
+  if ((int64_t)num_seqs * num_kv_heads * ((int64_t)max_blocks_per_seq + 16) > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs*num_kv_heads*max_blocks_per_seq too large");
   if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache |
        (uintptr_t)workspace) % 16 != 0)

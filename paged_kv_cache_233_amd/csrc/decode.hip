@@ -6,10 +6,12 @@
 // Attention Computation").
 //
 // Work split (split-KV, balanced): all (KV head g, sequence s, block j) tiles
-// form one index space ordered by g, then s, then j. The grid is a fixed
-// number W of single-wave workgroups; logical wave w takes the contiguous
-// tile range [w*T/W, (w+1)*T/W), T the total tile count, so every wave reads
-// the same number of K/V bytes whatever the length mix. Hardware workgroup b
+// form one index space ordered by g, then s, then j, in which every sequence
+// also counts a few units before its first block for the fixed cost of a
+// piece (below). The grid is a fixed number W of single-wave workgroups;
+// logical wave w takes the contiguous unit range [w*T/W, (w+1)*T/W), T the
+// total unit count, so every wave reads about the same number of K/V bytes
+// whatever the length mix. Hardware workgroup b
 // runs on XCD b % 8; logical waves are numbered so that each XCD owns one
 // contiguous eighth of the index space (one KV head when there are 8), which
 // keeps blocks shared between sequences (a common prefix) in one XCD's L2.
@@ -27,6 +29,10 @@
 // straight into registers and runs the MFMA tile step of tile_attn.h; the G
 // query heads of the group fill G of the 16 MFMA columns, the other columns
 // carry zero queries and are never stored.
+//
+// Append mode folds the cache write of the step's new token into the same
+// pass: the wave holding a sequence's last block writes the token's K and V
+// rows into it while staging its round, before it loads that block.
 #include <atomic>
 #include <cstdlib>
 #include <mutex>
@@ -60,6 +66,7 @@ struct DecodeParams {
   int32_t group;
   int32_t num_waves;
   int32_t pieces_per_round;  // pieces whose query rows fit the LDS budget
+  int32_t piece_cost;        // partition units a sequence costs besides its blocks
   float scale_log2;
   // Shared-prefix mode: every sequence's first `skip` blocks were attended
   // by the prefix phase, whose `pparts` softmax states per query row
@@ -70,6 +77,13 @@ struct DecodeParams {
   int32_t pparts;
   const float* pstate;
   int64_t pstride;
+  // Append mode (k_new != nullptr): before attending, the wave holding the
+  // block of a sequence's last position writes that position's key and
+  // value (k_new/v_new rows new_stride bytes apart, [num_kv_heads][D] each)
+  // into it, and its own later loads of the block read them back.
+  const char* k_new;
+  const char* v_new;
+  int64_t new_stride;
 };
 
 // Length of sequence s after clamping to [0, table width in tokens]; s may
@@ -244,18 +258,19 @@ struct Fold {
   }
 };
 
-// Fold the partial states of sequence s, KV head g (flat tiles first..last)
-// and write the normalised output. The owners of the sequence's tiles are
-// waves w0..w1 (in token order); merge wave k folds the contiguous quarter
-// [w0 + k*n/4, w0 + (k+1)*n/4) of them in order, each lane owning 8
-// consecutive output values of one query head and issuing the loads of
-// kMergeBatch states together; merge wave 0 then folds the four results in
-// order through LDS. The order is fixed, so the result is deterministic. A
-// wave whose range starts before the sequence holds its state in its second
-// slot, every other wave in its first.
+// Fold the partial states of sequence s, KV head g (units start..last, its
+// tiles first..last) and write the normalised output. The owners of the
+// sequence's tiles are waves w0..w1 (in token order); merge wave k folds the
+// contiguous quarter [w0 + k*n/4, w0 + (k+1)*n/4) of them in order, each lane
+// owning 8 consecutive output values of one query head and issuing the loads
+// of kMergeBatch states together; merge wave 0 then folds the four results
+// in order through LDS. The order is fixed, so the result is deterministic. A
+// wave whose range starts before the sequence's units finished a piece of an
+// earlier sequence first and holds its state in its second slot, every other
+// wave in its first.
 template <int DT, int D>
-__device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t first,
-                               int32_t last, const WaveRanges& R) {
+__device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t start,
+                               int32_t first, int32_t last, const WaveRanges& R) {
   __shared__ float xs[kMergeWaves - 1][10][64];
   const int lane = threadIdx.x & 63;
   const int mw = threadIdx.x >> 6;
@@ -278,7 +293,7 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
       int cnt = 0;
       for (; wv < wb && cnt < kMergeBatch; ++wv) {
         if (R.empty(wv)) continue;
-        slot[cnt++] = 2 * wv + (R.begin(wv) < first ? 1 : 0);
+        slot[cnt++] = 2 * wv + (R.begin(wv) < start ? 1 : 0);
       }
       float4 o0[kMergeBatch], o1[kMergeBatch];
       float mk[kMergeBatch], lk[kMergeBatch];
@@ -351,6 +366,7 @@ constexpr int32_t kFinal = 1;  // the wave's work on this sequence ends here
 constexpr int32_t kWhole = 2;  // the wave holds the whole sequence: store the output
 constexpr int32_t kFirst = 4;  // the sequence is the wave's first: partial state in slot 2w
 constexpr int32_t kCont = 8;   // continues the previous round's last piece: keep the state
+constexpr int32_t kTail = 16;  // holds the sequence's last block
 
 constexpr int kTilesPerRound = 512;
 constexpr int kPiecesPerRound = 16;
@@ -370,7 +386,8 @@ decode_split_kernel(DecodeParams p) {
   int32_t* tiles = reinterpret_cast<int32_t*>(lds);                       // [kTilesPerRound]
   int32_t* tile_head = tiles + kTilesPerRound;                            // [kTilesPerRound]
   Piece* pieces = reinterpret_cast<Piece*>(tile_head + kTilesPerRound);   // [kPiecesPerRound]
-  char* qlds = reinterpret_cast<char*>(pieces + kPiecesPerRound);         // [kq][G * kRow]
+  int32_t* tails = reinterpret_cast<int32_t*>(pieces + kPiecesPerRound);  // [kPiecesPerRound]
+  char* qlds = reinterpret_cast<char*>(tails + kPiecesPerRound);          // [kq][G * kRow]
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int kg = lane >> 4;
@@ -383,15 +400,21 @@ decode_split_kernel(DecodeParams p) {
   // Total tiles per head: scan the block counts in chunks of 64 sequences.
   // The first chunk's scan is kept: with up to 64 sequences it also serves
   // to locate the wave's first tile without reading the lengths again.
+  // The partition is over units, not tiles: a sequence with blocks counts
+  // piece_cost units before its blocks, the time a wave spends opening and
+  // closing a piece (staging its query rows, writing its state) measured in
+  // tiles streamed. A wave whose units are the cost units of a sequence takes
+  // no tile for them.
   int32_t per_head = 0;
-  int32_t nb0 = 0, incl0 = 0, len0 = 0;
+  int32_t nv0 = 0, incl0 = 0, len0 = 0;
   for (int32_t base = 0; base < p.num_seqs; base += 64) {
     const int32_t sq = base + lane;
     const int32_t len = sq < p.num_seqs ? seq_len_clamped(p, sq) : 0;
     const int32_t nb = (len + 15) >> 4;
-    const int32_t incl = wave_incl_scan(nb);
+    const int32_t nv = nb > 0 ? nb + p.piece_cost : 0;
+    const int32_t incl = wave_incl_scan(nv);
     if (base == 0) {
-      nb0 = nb;
+      nv0 = nv;
       incl0 = incl;
       len0 = len;
     }
@@ -416,32 +439,34 @@ decode_split_kernel(DecodeParams p) {
   const int32_t i1 = R.begin(w + 1);
   if (i0 >= i1) return;
 
-  // Locate the (head, sequence) holding tile i0.
+  // Locate the (head, sequence) holding unit i0.
   int32_t g = i0 / per_head;
   const int32_t r = i0 - g * per_head;
   int32_t s = 0, seq_start = 0, len_s = 0;
   {
     int32_t start = 0;
     for (int32_t base = 0; base < p.num_seqs; base += 64) {
-      int32_t nb = nb0, incl = incl0, len = len0;
+      int32_t nv = nv0, incl = incl0, len = len0;
       if (base > 0) {
         const int32_t sq = base + lane;
         len = sq < p.num_seqs ? seq_len_clamped(p, sq) : 0;
-        nb = (len + 15) >> 4;
-        incl = wave_incl_scan(nb);
+        const int32_t nb = (len + 15) >> 4;
+        nv = nb > 0 ? nb + p.piece_cost : 0;
+        incl = wave_incl_scan(nv);
       }
       const uint64_t hit = __ballot(start + incl > r);
       if (hit) {
         const int li = __builtin_ctzll(hit);
         s = base + li;
-        seq_start = start + __builtin_amdgcn_readlane(incl - nb, li);
+        seq_start = start + __builtin_amdgcn_readlane(incl - nv, li);
         len_s = __builtin_amdgcn_readlane(len, li);
         break;
       }
       start += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  int32_t j = r - seq_start;             // next block of sequence s to take
+  // next unit of sequence s to take: its cost units, then block u - piece_cost
+  int32_t u = r - seq_start;
 
   const uint32_t k_off = k_lane_offset<DT, D>(n, kg);
   const uint32_t v_off = v_lane_offset<DT, D>(n, kg);
@@ -456,13 +481,22 @@ decode_split_kernel(DecodeParams p) {
   int32_t open_j0 = 0;                   // first block the wave took of the open sequence
   while (i < i1) {
     // ---- build a round: pieces, their tiles and their query rows -------
-    int32_t nt = 0, np = 0;
+    int32_t nt = 0, np = 0, ntail = 0;
     __syncthreads();
     while (i < i1 && nt < kTilesPerRound && np < p.pieces_per_round) {
       const int32_t nb_s = (len_s + 15) >> 4;
-      const int32_t cnt = (int32_t)min((int64_t)min(nb_s - j, kTilesPerRound - nt), i1 - i);
+      const int32_t nv_s = nb_s > 0 ? nb_s + p.piece_cost : 0;
+      if (u < p.piece_cost && nv_s > 0) {     // the sequence's cost units: no tile
+        const int32_t c = (int32_t)min((int64_t)(p.piece_cost - u), i1 - i);
+        u += c;
+        i += c;
+      }
+      const int32_t j = u - p.piece_cost;     // next block of sequence s
+      const int32_t cnt = u < p.piece_cost ? 0
+          : (int32_t)min((int64_t)min(nb_s - j, kTilesPerRound - nt), i1 - i);
       if (cnt > 0) {
         const bool fin = j + cnt == nb_s || i + cnt == i1;
+        const bool tail = j + cnt == nb_s;
         if (!(cont && np == 0)) open_j0 = j;
         if (lane == 0) {
           Piece pc;
@@ -472,26 +506,29 @@ decode_split_kernel(DecodeParams p) {
           pc.kstart = nt;
           pc.kend = nt + cnt;
           pc.len = len_s;
-          pc.flags = (fin ? kFinal : 0) | (open_j0 == 0 && j + cnt == nb_s ? kWhole : 0) |
-                     (first ? kFirst : 0) | (cont && np == 0 ? kCont : 0);
+          pc.flags = (fin ? kFinal : 0) | (open_j0 == 0 && tail ? kWhole : 0) |
+                     (first ? kFirst : 0) | (cont && np == 0 ? kCont : 0) | (tail ? kTail : 0);
           pc.pad = 0;
           pieces[np] = pc;
+          if (tail) tails[ntail] = np;
         }
+        ntail += tail ? 1 : 0;
         // For now each tile holds its index in the block table (and its KV
         // head); the ids are read below, for all pieces at once.
         const int32_t tbase = s * p.max_blocks + p.skip + j;
         for (int32_t t = lane; t < cnt; t += 64) {
           tiles[nt + t] = tbase + t;
           tile_head[nt + t] = g;
-        }        ++np;
+        }
+        ++np;
         nt += cnt;
         i += cnt;
-        j += cnt;
+        u += cnt;
         cont = !fin;
         if (fin) first = false;
       }
-      if (j >= nb_s) {  // next sequence, wrapping to the next head
-        j = 0;
+      if (u >= nv_s) {  // next sequence, wrapping to the next head
+        u = 0;
         if (++s == p.num_seqs) {
           s = 0;
           ++g;
@@ -502,75 +539,119 @@ decode_split_kernel(DecodeParams p) {
         }
       }
     }
+    // (the range ended inside a sequence's cost units: nothing left to stream)
+    if (nt == 0) break;
     __syncthreads();
-    // Block ids of every tile of the round and the query rows of every piece
-    // (heads g*G .. g*G+G-1 of its sequence, contiguous): all loads of a
-    // batch are issued before anything is written, so the round's staging
-    // takes one memory round trip (one per 512 chunks of query rows).
+    // Staging, in batches: (a) read from LDS what the batch's loads need,
+    // (b) issue all its global loads -- in the first batch the block ids of
+    // every tile of the round, and in every batch up to 64*kQ chunks of the
+    // pieces' query rows (heads g*G .. g*G+G-1 of the sequence, contiguous)
+    // and, in append mode, up to 64*kN chunks of the new K/V rows -- (c) wait
+    // once, (d) write LDS and store the new rows. One memory round trip per
+    // batch; a round needs one batch unless it holds more than 64*kQ query
+    // chunks or 64*kN new-row chunks.
     {
-      int32_t bid[kTilesPerRound / 64];
-#pragma unroll
-      for (int m = 0; m < kTilesPerRound / 64; ++m) {
-        const int32_t k = lane + 64 * m;
-        bid[m] = k < nt ? p.block_table[tiles[k]] : 0;
-      }
-      const int32_t cpp = qbytes / 16;        // 16-byte chunks per piece
-      const int32_t nq = np * cpp;
-      constexpr int kQ = Sh::kRow > 256 ? 2 : 4;   // query chunks per lane and batch
+      constexpr int kB = kTilesPerRound / 64;     // block ids per lane
+      constexpr int kQ = Sh::kRow > 256 ? 2 : 4;  // query chunks per lane and batch
+      constexpr int kCpr = Sh::kRow / 16;         // 16-byte chunks per K or V row
+      constexpr int kN = 4;                       // new-row chunks per lane and batch
       // (a native vector type: the HIP uint4 class copies through memcpy,
       // which would put these registers in scratch memory)
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      for (int32_t c0 = 0; c0 < nq; c0 += 64 * kQ) {
-        // chunk c = c0 + lane + 64m is 16-byte chunk o of piece q; (q, o)
-        // advance by 64 chunks per m
-        u32x4 qc[kQ];
-        int32_t q = (c0 + lane) / cpp;
-        int32_t o = (c0 + lane) - q * cpp;
-        const int32_t q_first = q, o_first = o;
+      const int32_t cpp = qbytes / 16;            // query chunks per piece
+      const int32_t nq = np * cpp;
+      // new-row chunk c: chunk o of row kv (0 = K, 1 = V) of tail piece c / (2 kCpr)
+      const int32_t nn = p.k_new != nullptr ? ntail * 2 * kCpr : 0;
+      for (int32_t c0 = 0, n0 = 0; c0 == 0 || c0 < nq || n0 < nn; c0 += 64 * kQ, n0 += 64 * kN) {
+        const bool first_batch = c0 == 0;
+        // (a) addresses
+        int32_t tix[kB];
+        if (first_batch) {
 #pragma unroll
-        for (int m = 0; m < kQ; ++m) {
-          if (c0 + lane + 64 * m < nq) {
-            const Piece& P = pieces[q];
-            const char* qsrc = reinterpret_cast<const char*>(p.q) +
-                               ((int64_t)P.s * p.num_q_heads + (int64_t)P.g * G) * Sh::kRow;
-            qc[m] = *reinterpret_cast<const u32x4*>(qsrc + 16 * o);
-          }
-          o += 64;
-          while (o >= cpp) {
-            o -= cpp;
-            ++q;
+          for (int m = 0; m < kB; ++m) {
+            const int32_t k = lane + 64 * m;
+            tix[m] = k < nt ? tiles[k] : 0;
           }
         }
-        if (c0 == 0) {
+        const char* qsrc[kQ];
+        int32_t qdst[kQ];
 #pragma unroll
-          for (int m = 0; m < kTilesPerRound / 64; ++m) {
+        for (int m = 0; m < kQ; ++m) {
+          const int32_t c = c0 + lane + 64 * m;
+          const int32_t pi = c < nq ? c / cpp : 0;
+          const int32_t o = c - pi * cpp;
+          const Piece& P = pieces[pi];
+          qsrc[m] = reinterpret_cast<const char*>(p.q) +
+                    ((int64_t)P.s * p.num_q_heads + (int64_t)P.g * G) * Sh::kRow + 16 * o;
+          qdst[m] = pi * qbytes + 16 * o;
+        }
+        const char* nsrc[kN];
+        int32_t nlast[kN], nrow[kN];   // tile index of the row's block; byte offset in the tile
+#pragma unroll
+        for (int m = 0; m < kN; ++m) {
+          const int32_t c = n0 + lane + 64 * m;
+          const int32_t ti = c < nn ? c / (2 * kCpr) : 0;
+          const int32_t r = c - ti * 2 * kCpr;
+          const int32_t kv = r >= kCpr ? 1 : 0;
+          const int32_t o = r - kv * kCpr;
+          const Piece& P = pieces[c < nn ? tails[ti] : 0];
+          nsrc[m] = (kv ? p.v_new : p.k_new) + (int64_t)P.s * p.new_stride +
+                    (int64_t)P.g * Sh::kRow + 16 * o;
+          nlast[m] = P.kend - 1;
+          // bit 30 marks a V row (the offset itself is below 2^13)
+          nrow[m] = (((P.len - 1) & 15) * Sh::kRow + 16 * o) | (kv << 30);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (b) loads
+        int32_t bid[kB];
+        if (first_batch) {
+#pragma unroll
+          for (int m = 0; m < kB; ++m)
+            bid[m] = lane + 64 * m < nt ? p.block_table[tix[m]] : 0;
+        }
+        u32x4 qc[kQ], nc[kN];
+#pragma unroll
+        for (int m = 0; m < kQ; ++m)
+          if (c0 + lane + 64 * m < nq) qc[m] = *reinterpret_cast<const u32x4*>(qsrc[m]);
+#pragma unroll
+        for (int m = 0; m < kN; ++m)
+          if (n0 + lane + 64 * m < nn) nc[m] = *reinterpret_cast<const u32x4*>(nsrc[m]);
+        __builtin_amdgcn_sched_barrier(0);
+        // (d) LDS writes: pool tile of every tile of the round, query rows
+        if (first_batch) {
+#pragma unroll
+          for (int m = 0; m < kB; ++m) {
             const int32_t k = lane + 64 * m;
             if (k < nt)
               tiles[k] = ((uint32_t)bid[m] < (uint32_t)p.num_blocks ? bid[m] : 0) * p.num_kv_heads +
                          tile_head[k];
           }
         }
-        q = q_first;
-        o = o_first;
 #pragma unroll
-        for (int m = 0; m < kQ; ++m) {
-          if (c0 + lane + 64 * m < nq)
-            *reinterpret_cast<u32x4*>(qlds + q * qbytes + 16 * o) = qc[m];
-          o += 64;
-          while (o >= cpp) {
-            o -= cpp;
-            ++q;
+        for (int m = 0; m < kQ; ++m)
+          if (c0 + lane + 64 * m < nq) *reinterpret_cast<u32x4*>(qlds + qdst[m]) = qc[m];
+        // The new rows go to position len - 1 of their sequence: row
+        // (len - 1) % 16 of the tail piece's last tile, unless that tile is
+        // in block 0 (an id outside the pool, or the null block, which is
+        // never written). The tile loads of the round come after these
+        // stores in this wave's program order and read the same addresses,
+        // so they return the new rows; no other wave reads this
+        // (block, KV head).
+        char* ndst[kN];
+#pragma unroll
+        for (int m = 0; m < kN; ++m) {
+          ndst[m] = nullptr;
+          if (n0 + lane + 64 * m < nn) {
+            const int32_t t = tiles[nlast[m]];
+            if (t >= p.num_kv_heads)
+              ndst[m] = const_cast<char*>((nrow[m] >> 30) ? p.v_cache : p.k_cache) +
+                        (int64_t)t * Sh::kTileBytes + (nrow[m] & ((1 << 30) - 1));
           }
         }
-      }
-      if (nq == 0) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < kTilesPerRound / 64; ++m) {
-          const int32_t k = lane + 64 * m;
-          if (k < nt)
-            tiles[k] = ((uint32_t)bid[m] < (uint32_t)p.num_blocks ? bid[m] : 0) * p.num_kv_heads +
-                       tile_head[k];
-        }
+        for (int m = 0; m < kN; ++m)
+          if (ndst[m] != nullptr) *reinterpret_cast<u32x4*>(ndst[m]) = nc[m];
       }
     }
     __syncthreads();
@@ -655,10 +736,11 @@ decode_merge_kernel(DecodeParams p) {
   const int32_t b = p.ws_prefix[s + 1];
   if (a == b) return;
   const WaveRanges R(per_head * p.num_kv_heads, p.num_waves);
-  const int32_t first = g * per_head + a;
-  const int32_t last = g * per_head + b - 1;
+  const int32_t start = g * per_head + a;          // the sequence's first (cost) unit
+  const int32_t first = start + p.piece_cost;      // its first tile
+  const int32_t last = g * per_head + b - 1;       // its last tile
   if (R.owner(first) == R.owner(last)) return;
-  merge_sequence<DT, D>(p, s, g, first, last, R);
+  merge_sequence<DT, D>(p, s, g, start, first, last, R);
 }
 
 // Launch settings, read by every decode call and possibly from several host
@@ -667,6 +749,23 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_waves[kMaxDevices];
 std::atomic<int> g_waves_per_cu{0};   // set by decode_set_waves_per_cu; 0 = default
 std::atomic<int> g_depth{0};
+
+// Partition units a sequence costs besides its blocks (see the split
+// kernel); PKV_DECODE_PIECE_COST overrides it (0..8) for tuning.
+std::atomic<int> g_piece_cost{-1};
+
+int decode_piece_cost() {
+  int c = g_piece_cost.load(std::memory_order_relaxed);
+  if (c < 0) {
+    c = 2;
+    if (const char* env = getenv("PKV_DECODE_PIECE_COST")) {
+      int v = atoi(env);
+      if (v >= 0 && v <= 8) c = v;
+    }
+    g_piece_cost.store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
 
 int decode_depth() {
   int d = g_depth.load(std::memory_order_relaxed);
@@ -684,7 +783,7 @@ int decode_depth() {
 // Dynamic LDS of the split kernel: tile list, pieces, query rows.
 template <int DT, int D>
 size_t split_lds_bytes(const DecodeParams& prm) {
-  return (size_t)kTilesPerRound * 8 + kPiecesPerRound * sizeof(Piece) +
+  return (size_t)kTilesPerRound * 8 + kPiecesPerRound * (sizeof(Piece) + 4) +
          (size_t)prm.pieces_per_round * prm.group * Shape<DT, D>::kRow;
 }
 
@@ -797,6 +896,9 @@ static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const fl
   p.pstate = pstate;
   p.pparts = pparts;
   p.pstride = (int64_t)a.num_seqs * a.num_q_heads * (a.head_dim + 4);
+  p.k_new = reinterpret_cast<const char*>(a.k_new);
+  p.v_new = reinterpret_cast<const char*>(a.v_new);
+  p.new_stride = a.new_token_stride * (a.dtype == PKV_F32 ? 4 : 2);
   p.out = a.out;
   p.q = a.q;
   p.k_cache = reinterpret_cast<const char*>(a.k_cache);
@@ -813,6 +915,7 @@ static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const fl
   p.num_kv_heads = a.num_kv_heads;
   p.group = a.num_q_heads / a.num_kv_heads;
   p.num_waves = decode_num_waves();
+  p.piece_cost = decode_piece_cost();
   p.scale_log2 = a.scale * kLog2e;
   {
     // query rows of up to 16 pieces per round, within 16 KiB of LDS

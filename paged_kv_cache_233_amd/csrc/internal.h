@@ -47,6 +47,12 @@ struct DecodeArgs {
   float scale;
   int32_t dtype;
   void* workspace;
+  // Append mode: each sequence's current token (k_new/v_new rows, tokens
+  // new_token_stride elements apart) is written into the cache by the
+  // split-KV kernel itself before it attends; nullptr = plain decode.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int64_t new_token_stride = 0;
 };
 
 // Number of waves the split-KV decode kernel is launched with on the current

@@ -63,7 +63,10 @@ class KVCache:
 
 
 def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
-               prefill: bool = True) -> dict:
+               prefill: bool = True, fused_append: bool = False) -> dict:
+    """``fused_append``: the decode sequences' new tokens are not scattered
+    by reshape_and_cache but written by the decode itself (decode_append);
+    the chunks' tokens still go through reshape_and_cache."""
     import paged_kv_cache_233_amd as pkv
 
     dt = w.torch_dtype
@@ -98,15 +101,19 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
     if pairs:
         pkv.copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device=device))
         res_pairs.extend(pairs)
-    ks, vs = [], []
+    ks, vs, keep = [], [], []
     for sid, n in zip(ids, ns):
         k, v = kv.get(sid)
         spec = kv.specs[sid]
-        ks.append(k[spec.cached:spec.total])
-        vs.append(v[spec.cached:spec.total])
-    if ids:
+        fused = fused_append and not spec.is_chunk
+        keep += [not fused] * n
+        if not fused:
+            ks.append(k[spec.cached:spec.total])
+            vs.append(v[spec.cached:spec.total])
+    if ks:
+        sl = slots[np.array(keep, dtype=bool)]
         pkv.reshape_and_cache(kc, vc, torch.cat(ks).to(device), torch.cat(vs).to(device),
-                              torch.from_numpy(slots).to(device))
+                              torch.from_numpy(np.ascontiguousarray(sl)).to(device))
     res = {"step_slots": slots, "cow_pairs": res_pairs}
     dec = w.decode_seqs
     maxb = w.max_blocks_per_seq()
@@ -116,8 +123,21 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
         q = torch.cat([w.seq_q(s) for s in dec]).to(device)
         out = torch.empty_like(q)
         ws = pkv.decode_workspace(len(dec), w.num_q_heads, w.num_kv_heads, w.head_dim, device)
-        pkv.decode(out, q, kc, vc, torch.from_numpy(table).to(device),
-                   torch.from_numpy(lens).to(device), w.scale, ws)
+        if fused_append:
+            # one new K/V row per decode sequence (zeros for an empty one,
+            # which has no position to write)
+            k_new = torch.zeros((len(dec), w.num_kv_heads, w.head_dim), dtype=dt)
+            v_new = torch.zeros_like(k_new)
+            for i, spec in enumerate(dec):
+                if spec.new_tokens:
+                    k, v = kv.get(spec.seq_id)
+                    k_new[i], v_new[i] = k[spec.total - 1], v[spec.total - 1]
+            pkv.decode_append(out, q, k_new.to(device), v_new.to(device), kc, vc,
+                              torch.from_numpy(table).to(device), torch.from_numpy(lens).to(device),
+                              w.scale, ws)
+        else:
+            pkv.decode(out, q, kc, vc, torch.from_numpy(table).to(device),
+                       torch.from_numpy(lens).to(device), w.scale, ws)
         res["decode"] = out
         res["decode_table"] = table
         res["decode_lens"] = lens
