@@ -287,15 +287,25 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_c
                       scratch, (size_t)PKV_DECODE_SCRATCH_BYTES, stream, 3);
 }
 
-// Workspace of the shared-prefix decode: the decode workspace, then the
-// prefix states (parts x num_seqs x num_q_heads x (head_dim + 4) floats),
-// which the decode folds at each sequence's first piece.
-static size_t shared_prefix_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t prefix_blocks, int32_t* parts) {
-  const size_t dec = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
-                      255) / 256 * 256;
-  *parts = pkv::prefix_state_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks * 16);
-  return dec + (size_t)*parts * num_seqs * num_q_heads * (head_dim + 4) * 4;
+// Workspace of the shared-prefix decode: the decode workspace; the states
+// of the sequences one wave holds whole (num_seqs x num_kv_heads x G x
+// (head_dim + 4) floats); then the prefix states (parts x num_seqs x
+// num_q_heads x (head_dim + 4) floats), which the merge folds first.
+struct SharedLayout {
+  size_t decode, whole, state, total;
+  int32_t parts;
+};
+static SharedLayout shared_prefix_layout(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t prefix_blocks) {
+  SharedLayout l;
+  l.decode = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) + 255) /
+             256 * 256;
+  l.whole = ((size_t)num_seqs * num_q_heads * (head_dim + 4) * 4 + 255) / 256 * 256;
+  l.parts = pkv::prefix_state_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks * 16);
+  l.state = (size_t)l.parts * num_seqs * num_q_heads * (head_dim + 4) * 4;
+  l.total = l.decode + l.whole + l.state;
+  return l;
 }
 
 int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -307,8 +317,7 @@ int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_head
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
   if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d", head_dim);
   if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
-  int32_t parts;
-  *out = shared_prefix_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_blocks, &parts);
+  *out = shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, prefix_blocks).total;
   return PKV_OK;
 }
 
@@ -342,25 +351,24 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
        (uintptr_t)workspace) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "q, out, pools and workspace must be 16-byte aligned");
   if (pkv::decode_num_waves() <= 0) return fail(PKV_ERR_HIP, "no HIP device");
-  int32_t parts;
-  const size_t need = shared_prefix_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                          prefix_blocks, &parts);
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "shared-prefix decode needs %zu workspace bytes, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  const size_t dec = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
-                      255) / 256 * 256;
-  float* state = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec);
+  const SharedLayout l = shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              prefix_blocks);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(PKV_ERR_WORKSPACE, "shared-prefix decode needs %zu workspace bytes, got %zu",
+                l.total, workspace ? workspace_bytes : (size_t)0);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* whole = reinterpret_cast<float*>(ws + l.decode);
+  float* state = reinterpret_cast<float*>(ws + l.decode + l.whole);
   pkv::PrefillArgs pa{nullptr, q, nullptr, nullptr, block_table, k_cache, v_cache, 1, num_seqs,
                       num_blocks, max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads,
                       head_dim, scale, dtype};
-  hipError_t err = pkv::launch_prefix_state(pa, prefix_blocks * 16, parts, state,
-                                            (hipStream_t)stream);
-  if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix phase launch");
   pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                     max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                     workspace};
-  err = pkv::launch_decode_after_prefix(a, prefix_blocks, state, parts, 3, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t err = pkv::launch_prefix_state(pa, prefix_blocks * 16, l.parts, state, st);
+  if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix phase launch");
+  err = pkv::launch_decode_after_prefix(a, prefix_blocks, state, l.parts, 3, st, whole);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
 }
 

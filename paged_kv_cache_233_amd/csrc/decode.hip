@@ -71,12 +71,16 @@ struct DecodeParams {
   // Shared-prefix mode: every sequence's first `skip` blocks were attended
   // by the prefix phase, whose `pparts` softmax states per query row
   // (pstate[part * pstride + row * (D + 4)]: O[D], max (log2 units), sum, two
-  // floats of padding that keep every row 16-byte aligned)
-  // start the sequence's state. skip = 0 and pstate = nullptr otherwise.
+  // floats of padding that keep every row 16-byte aligned) the merge kernel
+  // folds before the sequence's own states. The split kernel then writes no
+  // output: it leaves the state of a sequence one wave holds whole in
+  // ws_whole[s * num_kv_heads + g] (G x (D + 4) floats), and the merge kernel
+  // writes every output. skip = 0 and pstate = nullptr otherwise.
   int32_t skip;
   int32_t pparts;
   const float* pstate;
   int64_t pstride;
+  float* ws_whole;
   // Append mode (k_new != nullptr): before attending, the wave holding the
   // block of a sequence's last position writes that position's key and
   // value (k_new/v_new rows new_stride bytes apart, [num_kv_heads][D] each)
@@ -114,11 +118,10 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
 }
 
 template <int DT, int D>
-__device__ __forceinline__ void write_partial(const DecodeParams& p, const State<DT, D>& st,
-                                              int32_t slot, int n, int kg) {
+__device__ __forceinline__ void write_state(const DecodeParams& p, const State<DT, D>& st,
+                                            float* base, int n, int kg) {
   using Sh = Shape<DT, D>;
   if (n >= p.group) return;
-  float* base = p.ws_partial + (int64_t)slot * p.group * (D + 4);
   float* o = base + n * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -131,6 +134,12 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, const State
     base[p.group * D + n] = st.m;
     base[p.group * D + p.group + n] = st.l;
   }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, const State<DT, D>& st,
+                                              int32_t slot, int n, int kg) {
+  write_state<DT, D>(p, st, p.ws_partial + (int64_t)slot * p.group * (D + 4), n, kg);
 }
 
 // The waves' flat tile ranges: wave w takes [begin(w), begin(w + 1)) with
@@ -157,66 +166,6 @@ struct WaveRanges {
     return w;
   }
 };
-
-// Softmax state of query row `row` folded from the prefix states: lane
-// (n, kg) of the tile layout gets dims (4kg + i) * (D/16) + e.
-template <int DT, int D>
-__device__ __forceinline__ void prefix_init(const DecodeParams& p, State<DT, D>& st, int64_t row,
-                                            int kg) {
-  using Sh = Shape<DT, D>;
-  float m = -INFINITY;
-  for (int32_t k = 0; k < p.pparts; ++k) m = fmaxf(m, p.pstate[k * p.pstride + row * (D + 4) + D]);
-  st.m = m;
-  st.l = 0.f;
-#pragma unroll
-  for (int e = 0; e < Sh::kTiles; ++e) st.o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int32_t k = 0; k < p.pparts; ++k) {
-    const float* src = p.pstate + k * p.pstride + row * (D + 4);
-    const float wk = __builtin_amdgcn_exp2f(src[D] - m);
-    st.l += src[D + 1] * wk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float* od = src + (4 * kg + i) * Sh::kTiles;
-#pragma unroll
-      for (int e = 0; e < Sh::kTiles; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(od + e);
-        st.o[e][i] += v.x * wk;
-        st.o[e + 1][i] += v.y * wk;
-        st.o[e + 2][i] += v.z * wk;
-        st.o[e + 3][i] += v.w * wk;
-      }
-    }
-  }
-}
-
-// Output of a sequence with nothing after the shared prefix: its prefix
-// states folded and normalised (all query heads).
-template <int DT, int D>
-__device__ __forceinline__ void prefix_rows(const DecodeParams& p, int32_t s) {
-  for (int32_t h = 0; h < p.num_q_heads; ++h) {
-    const int64_t row = (int64_t)s * p.num_q_heads + h;
-    float m = -INFINITY;
-    for (int32_t k = 0; k < p.pparts; ++k) m = fmaxf(m, p.pstate[k * p.pstride + row * (D + 4) + D]);
-    float l = 0.f;
-    for (int32_t k = 0; k < p.pparts; ++k) {
-      const float* src = p.pstate + k * p.pstride + row * (D + 4);
-      l += src[D + 1] * __builtin_amdgcn_exp2f(src[D] - m);
-    }
-    for (int32_t d = threadIdx.x; d < D; d += 64) {
-      float o = 0.f;
-      for (int32_t k = 0; k < p.pparts; ++k) {
-        const float* src = p.pstate + k * p.pstride + row * (D + 4);
-        o += src[d] * __builtin_amdgcn_exp2f(src[D] - m);
-      }
-      o /= l;
-      if constexpr (DT == PKV_BF16) {
-        reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)o;
-      } else {
-        reinterpret_cast<float*>(p.out)[row * D + d] = o;
-      }
-    }
-  }
-}
 
 // Zero output of an empty sequence (all query heads).
 template <int DT, int D>
@@ -258,16 +207,76 @@ struct Fold {
   }
 };
 
+// Fold, in order, the partial states that the non-empty waves of [wa, wb)
+// hold for the sequence whose units start at `start`: lane values e .. e+7
+// (query head h of the group). A wave whose range starts before the
+// sequence's units finished a piece of an earlier sequence first and holds
+// its state in its second slot, every other wave in its first. The loads of
+// kMergeBatch states are issued together.
+template <int D>
+__device__ __forceinline__ void fold_owners(const DecodeParams& p, const WaveRanges& R, int32_t wa,
+                                            int32_t wb, int32_t start, int32_t e, int32_t h,
+                                            Fold& f) {
+  const int32_t G = p.group;
+  const int32_t stride = G * (D + 4);
+  int32_t wv = wa;
+  while (wv < wb) {
+    int32_t slot[kMergeBatch];
+    int cnt = 0;
+    for (; wv < wb && cnt < kMergeBatch; ++wv) {
+      if (R.empty(wv)) continue;
+      slot[cnt++] = 2 * wv + (R.begin(wv) < start ? 1 : 0);
+    }
+    float4 o0[kMergeBatch], o1[kMergeBatch];
+    float mk[kMergeBatch], lk[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k < cnt) {
+        const float* base = p.ws_partial + (int64_t)slot[k] * stride;
+        o0[k] = *reinterpret_cast<const float4*>(base + e);
+        o1[k] = *reinterpret_cast<const float4*>(base + e + 4);
+        mk[k] = base[G * D + h];
+        lk[k] = base[G * D + G + h];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (k < cnt) {
+        const float ov[8] = {o0[k].x, o0[k].y, o0[k].z, o0[k].w, o1[k].x, o1[k].y, o1[k].z, o1[k].w};
+        f.add(mk[k], lk[k], ov);
+      }
+    }
+  }
+}
+
+// Normalised values e .. e+7 of the output rows starting at out_row.
+template <int DT, int D>
+__device__ __forceinline__ void store_folded(const DecodeParams& p, const Fold& f, int64_t out_row,
+                                             int32_t e) {
+  const float inv = 1.0f / f.den;
+  if constexpr (DT == PKV_BF16) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      bf16x2 v = {(__bf16)(f.num[i] * inv), (__bf16)(f.num[i + 1] * inv)};
+      wd[i / 2] = __builtin_bit_cast(uint32_t, v);
+    }
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + out_row + e) =
+        uint4{wd[0], wd[1], wd[2], wd[3]};
+  } else {
+    float* o = reinterpret_cast<float*>(p.out) + out_row + e;
+    *reinterpret_cast<float4*>(o) = float4{f.num[0] * inv, f.num[1] * inv, f.num[2] * inv, f.num[3] * inv};
+    *reinterpret_cast<float4*>(o + 4) = float4{f.num[4] * inv, f.num[5] * inv, f.num[6] * inv, f.num[7] * inv};
+  }
+}
+
 // Fold the partial states of sequence s, KV head g (units start..last, its
 // tiles first..last) and write the normalised output. The owners of the
 // sequence's tiles are waves w0..w1 (in token order); merge wave k folds the
 // contiguous quarter [w0 + k*n/4, w0 + (k+1)*n/4) of them in order, each lane
 // owning 8 consecutive output values of one query head and issuing the loads
 // of kMergeBatch states together; merge wave 0 then folds the four results
-// in order through LDS. The order is fixed, so the result is deterministic. A
-// wave whose range starts before the sequence's units finished a piece of an
-// earlier sequence first and holds its state in its second slot, every other
-// wave in its first.
+// in order through LDS. The order is fixed, so the result is deterministic.
 template <int DT, int D>
 __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int32_t start,
                                int32_t first, int32_t last, const WaveRanges& R) {
@@ -280,41 +289,13 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
   const int32_t nw = w1 - w0 + 1;
   const int32_t wa = w0 + (mw * nw) / kMergeWaves;
   const int32_t wb = w0 + ((mw + 1) * nw) / kMergeWaves;
-  const int32_t stride = G * (D + 4);
   for (int32_t e0 = 0; e0 < G * D; e0 += 512) {
     const int32_t e = e0 + 8 * lane;
     const bool act = e < G * D;
     const int32_t h = act ? e / D : 0;
     Fold f;
     f.reset();
-    int32_t wv = wa;
-    while (act && wv < wb) {
-      int32_t slot[kMergeBatch];
-      int cnt = 0;
-      for (; wv < wb && cnt < kMergeBatch; ++wv) {
-        if (R.empty(wv)) continue;
-        slot[cnt++] = 2 * wv + (R.begin(wv) < start ? 1 : 0);
-      }
-      float4 o0[kMergeBatch], o1[kMergeBatch];
-      float mk[kMergeBatch], lk[kMergeBatch];
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        if (k < cnt) {
-          const float* base = p.ws_partial + (int64_t)slot[k] * stride;
-          o0[k] = *reinterpret_cast<const float4*>(base + e);
-          o1[k] = *reinterpret_cast<const float4*>(base + e + 4);
-          mk[k] = base[G * D + h];
-          lk[k] = base[G * D + G + h];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        if (k < cnt) {
-          const float ov[8] = {o0[k].x, o0[k].y, o0[k].z, o0[k].w, o1[k].x, o1[k].y, o1[k].z, o1[k].w};
-          f.add(mk[k], lk[k], ov);
-        }
-      }
-    }
+    if (act) fold_owners<D>(p, R, wa, wb, start, e, h, f);
     if (mw > 0) {
       xs[mw - 1][0][lane] = f.mx;
       xs[mw - 1][1][lane] = f.den;
@@ -331,21 +312,78 @@ __device__ void merge_sequence(const DecodeParams& p, int32_t s, int32_t g, int3
         // (an empty quarter has max -inf and sum 0: weight 0)
         if (xs[k][0][lane] != -INFINITY) f.add(xs[k][0][lane], xs[k][1][lane], ov);
       }
-      const float inv = 1.0f / f.den;
-      if constexpr (DT == PKV_BF16) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          bf16x2 v = {(__bf16)(f.num[i] * inv), (__bf16)(f.num[i + 1] * inv)};
-          wd[i / 2] = __builtin_bit_cast(uint32_t, v);
-        }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + out_row + e) =
-            uint4{wd[0], wd[1], wd[2], wd[3]};
-      } else {
-        float* o = reinterpret_cast<float*>(p.out) + out_row + e;
-        *reinterpret_cast<float4*>(o) = float4{f.num[0] * inv, f.num[1] * inv, f.num[2] * inv, f.num[3] * inv};
-        *reinterpret_cast<float4*>(o + 4) = float4{f.num[4] * inv, f.num[5] * inv, f.num[6] * inv, f.num[7] * inv};
+      store_folded<DT, D>(p, f, out_row, e);
+    }
+    __syncthreads();   // the LDS slots are reused by the next chunk of values
+  }
+}
+
+// Merge of sequence s, KV head g in shared-prefix mode: the prefix parts in
+// position order, then the suffix's
+// states in token order (units a..b of the head; none when a == b): the state
+// in ws_whole when one wave held the whole suffix, else the owners' partial
+// states, a contiguous quarter per merge wave as in merge_sequence. Merge wave
+// 0 folds the prefix before its quarter; the order is fixed.
+template <int DT, int D>
+__device__ void merge_with_prefix(const DecodeParams& p, int32_t s, int32_t g, int32_t a,
+                                  int32_t b, int32_t per_head, const WaveRanges& R) {
+  __shared__ float xs[kMergeWaves - 1][10][64];
+  const int lane = threadIdx.x & 63;
+  const int mw = threadIdx.x >> 6;
+  const int32_t G = p.group;
+  const int64_t out_row = ((int64_t)s * p.num_q_heads + (int64_t)g * G) * D;
+  int32_t start = 0, w0 = 0, nw = 0;
+  bool whole = false;
+  if (a < b) {
+    start = g * per_head + a;
+    w0 = R.owner(start + p.piece_cost);
+    const int32_t w1 = R.owner(g * per_head + b - 1);
+    whole = w0 == w1;
+    nw = whole ? 0 : w1 - w0 + 1;
+  }
+  const int32_t wa = w0 + (mw * nw) / kMergeWaves;
+  const int32_t wb = w0 + ((mw + 1) * nw) / kMergeWaves;
+  for (int32_t e0 = 0; e0 < G * D; e0 += 512) {
+    const int32_t e = e0 + 8 * lane;
+    const bool act = e < G * D;
+    const int32_t h = act ? e / D : 0;
+    Fold f;
+    f.reset();
+    if (act && mw == 0) {
+      const float* row = p.pstate + ((int64_t)s * p.num_q_heads + g * G + h) * (D + 4);
+      for (int32_t k = 0; k < p.pparts; ++k) {
+        const float* src = row + k * p.pstride;
+        const float4 o0 = *reinterpret_cast<const float4*>(src + (e - h * D));
+        const float4 o1 = *reinterpret_cast<const float4*>(src + (e - h * D) + 4);
+        const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        f.add(src[D], src[D + 1], ov);
       }
+      if (whole) {
+        const float* base = p.ws_whole + ((int64_t)s * p.num_kv_heads + g) * G * (D + 4);
+        const float4 o0 = *reinterpret_cast<const float4*>(base + e);
+        const float4 o1 = *reinterpret_cast<const float4*>(base + e + 4);
+        const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        f.add(base[G * D + h], base[G * D + G + h], ov);
+      }
+    }
+    if (act && nw > 0) fold_owners<D>(p, R, wa, wb, start, e, h, f);
+    if (mw > 0) {
+      xs[mw - 1][0][lane] = f.mx;
+      xs[mw - 1][1][lane] = f.den;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[mw - 1][2 + i][lane] = f.num[i];
+    }
+    __syncthreads();
+    if (mw == 0 && act) {
+#pragma unroll
+      for (int k = 0; k < kMergeWaves - 1; ++k) {
+        float ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ov[i] = xs[k][2 + i][lane];
+        // (an empty quarter has max -inf and sum 0: weight 0)
+        if (xs[k][0][lane] != -INFINITY) f.add(xs[k][0][lane], xs[k][1][lane], ov);
+      }
+      store_folded<DT, D>(p, f, out_row, e);
     }
     __syncthreads();   // the LDS slots are reused by the next chunk of values
   }
@@ -421,15 +459,13 @@ decode_split_kernel(DecodeParams p) {
     if (hw == 0) {
       if (sq < p.num_seqs) p.ws_prefix[sq + 1] = per_head + incl;
       if (base == 0 && lane == 0) p.ws_prefix[0] = 0;
-      // Empty sequences own no tile: this wave writes their zero output.
-      uint64_t empty = __ballot(sq < p.num_seqs && len == 0);
+      // Empty sequences own no tile: this wave writes their zero output
+      // (the merge writes it in shared-prefix mode).
+      uint64_t empty = p.pstate != nullptr ? 0 : __ballot(sq < p.num_seqs && len == 0);
       while (empty) {
         const int li = __builtin_ctzll(empty);
         empty &= empty - 1;
-        if (p.pstate != nullptr)
-          prefix_rows<DT, D>(p, base + li);
-        else
-          zero_rows<DT, D>(p, base + li);
+        zero_rows<DT, D>(p, base + li);
       }
     }
     per_head += __builtin_amdgcn_readlane(incl, 63);
@@ -681,10 +717,6 @@ decode_split_kernel(DecodeParams p) {
             qv[0].c[c] = n < G ? *reinterpret_cast<const uint4*>(qrow + 64 * c + 16 * kg)
                                : uint4{0u, 0u, 0u, 0u};
           st[0].reset();
-          // the sequence's first tile after a shared prefix: start from the
-          // prefix states (once per sequence and KV head)
-          if (p.pstate != nullptr && j0 == 0 && n < G)
-            prefix_init<DT, D>(p, st[0], (int64_t)ps * p.num_q_heads + pg * G + n, kg);
         }
       }
       const int32_t t0 = 16 * (j0 + k - kstart);
@@ -692,7 +724,10 @@ decode_split_kernel(DecodeParams p) {
       const int lim[1] = {end - 1};
       attend_tile<DT, D, 1>(st, tl, qv, p.scale_log2, t0, lim, end, end < t0 + 16, kg);
       if (k == kend - 1 && (pflags & kFinal)) {
-        if (pflags & kWhole)
+        if ((pflags & kWhole) && p.pstate != nullptr)
+          write_state<DT, D>(p, st[0], p.ws_whole + ((int64_t)ps * p.num_kv_heads + pg) * G * (D + 4),
+                             n, kg);
+        else if (pflags & kWhole)
           store_row<DT, D>(p.out, (int64_t)ps * p.num_q_heads + pg * G + n, st[0], kg, n < G);
         else
           write_partial<DT, D>(p, st[0], 2 * w + ((pflags & kFirst) ? 0 : 1), n, kg);
@@ -734,6 +769,11 @@ decode_merge_kernel(DecodeParams p) {
   const int32_t per_head = p.ws_prefix[p.num_seqs];
   const int32_t a = p.ws_prefix[s];
   const int32_t b = p.ws_prefix[s + 1];
+  if (p.pstate != nullptr) {
+    const WaveRanges R(max(per_head, 1) * p.num_kv_heads, p.num_waves);
+    merge_with_prefix<DT, D>(p, s, g, a, b, per_head, R);
+    return;
+  }
   if (a == b) return;
   const WaveRanges R(per_head * p.num_kv_heads, p.num_waves);
   const int32_t start = g * per_head + a;          // the sequence's first (cost) unit
@@ -890,11 +930,13 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
 }
 
 static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const float* pstate,
-                                     int32_t pparts, int phases, hipStream_t stream) {
+                                     int32_t pparts, int phases, hipStream_t stream,
+                                     float* whole_states = nullptr) {
   DecodeParams p;
   p.skip = skip;
   p.pstate = pstate;
   p.pparts = pparts;
+  p.ws_whole = whole_states;
   p.pstride = (int64_t)a.num_seqs * a.num_q_heads * (a.head_dim + 4);
   p.k_new = reinterpret_cast<const char*>(a.k_new);
   p.v_new = reinterpret_cast<const char*>(a.v_new);
@@ -937,8 +979,8 @@ hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
 
 hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
                                       const float* prefix_state, int32_t parts, int phases,
-                                      hipStream_t stream) {
-  return launch_decode_impl(a, skip_blocks, prefix_state, parts, phases, stream);
+                                      hipStream_t stream, float* whole_states) {
+  return launch_decode_impl(a, skip_blocks, prefix_state, parts, phases, stream, whole_states);
 }
 
 }  // namespace pkv

@@ -68,12 +68,14 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
 hipError_t decode_scratch(void** out);
 // phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.
 hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream);
-// Decode over each sequence's blocks from `skip_blocks` on, starting every
-// sequence's softmax state from the `parts` prefix states (see
-// launch_prefix_state) instead of from nothing.
+// Decode over each sequence's blocks from `skip_blocks` on, the merge kernel
+// folding the `parts` prefix states (see launch_prefix_state) before each
+// sequence's own states. whole_states: num_seqs x num_kv_heads states of
+// G x (head_dim + 4) floats, where the split kernel leaves the state of a
+// sequence whose blocks one wave holds whole.
 hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
                                       const float* prefix_state, int32_t parts, int phases,
-                                      hipStream_t stream);
+                                      hipStream_t stream, float* whole_states);
 
 struct PrefillArgs {
   void* out;

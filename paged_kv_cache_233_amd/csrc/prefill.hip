@@ -832,12 +832,11 @@ int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
                        int32_t prefix_tokens) {
   // About one workgroup per two CUs: (row blocks x KV heads) x parts, each
   // part keeping at least two 32-position tiles. With fewer workgroups than
-  // two per CU each runs eight waves over two halves of its positions. Fewer
-  // parts leave fewer partial states for the decode to fold at each
-  // sequence's start, and past about half the CUs the extra parallelism no
-  // longer pays for them (the whole shared-prefix decode of 128 sequences
-  // over a 2048-token prefix: 2 parts 58.6 us, 3 parts 56.7, 4 parts 56.9,
-  // 6 parts 61.2, 8 parts 64.6).
+  // two per CU each runs eight waves over two halves of its positions. Every
+  // part is one more state for the merge to fold per query row, and past
+  // about half the CUs the extra parallelism no longer pays for it (the whole
+  // shared-prefix decode of 128 sequences over a 2048-token prefix: 2 parts
+  // 57.1 us, 4 parts 51.8, 8 parts 52.1).
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t wg_tokens = kWaves * 2 * (16 / group);
   const int64_t base = (int64_t)((num_seqs + wg_tokens - 1) / wg_tokens) * num_kv_heads;
