@@ -89,3 +89,78 @@ def test_decode_step_graph_replays_equal_eager():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
         assert torch.equal(kc.view(torch.int16), kc_ref.view(torch.int16)), rep
         assert torch.equal(vc.view(torch.int16), vc_ref.view(torch.int16)), rep
+
+
+def test_decode_append_step_graph_replays_equal_oracle():
+    """The step with the new token's cache write folded into the decode
+    (index staging, split kernel with the write, merge) captured once and
+    replayed with new inputs: every replay writes each sequence's token at
+    position len - 1 through its table, as the oracle's scatter does, and
+    attends over the updated pools."""
+    print("[gpu] graph capture of a decode_append step", flush=True)
+    w = workloads.custom("gra", 61, [900, 64, 1300, 17, 2049], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    nat = run_native(w, prefill=False)
+    ora = run_oracle(w, prefill=False)
+    ok, ov = ora["k_cache"].copy(), ora["v_cache"].copy()
+    dec = w.decode_seqs
+    S = len(dec)
+    table, lens = nat["decode_table"], nat["decode_lens"]
+    maxb = table.shape[1]
+    words = (S + S * maxb + 1) // 2
+    pinned = torch.zeros(words, dtype=torch.int64).pin_memory()
+    stage = torch.empty(words, dtype=torch.int64, device="cuda")
+    q = torch.empty((S, 32, 128), dtype=torch.bfloat16, device="cuda")
+    k_new = torch.empty((S, 8, 128), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.empty_like(k_new)
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(S, 32, 8, 128)
+    kc, vc = nat["k_cache"].clone(), nat["v_cache"].clone()
+
+    def fill(ln):
+        p32 = pinned.view(torch.int32)
+        p32[:S] = torch.from_numpy(ln)
+        p32[S:S + S * maxb] = torch.from_numpy(table.reshape(-1))
+
+    def step(kc_, vc_, out_):
+        pkv.stage_copy(stage, pinned)
+        st32 = stage.view(torch.int32)
+        pkv.decode_append(out_, q, k_new, v_new, kc_, vc_, st32[S:S + S * maxb].view(S, maxb),
+                          st32[:S], w.scale, ws)
+
+    rng = np.random.default_rng(1)
+    g = torch.cuda.CUDAGraph()
+    fill(lens)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step(kc, vc, out)
+    torch.cuda.synchronize()
+    # the capture ran nothing: the pools still hold the setup
+    assert to_numpy_storage(kc).tobytes() == ok.tobytes()
+    for rep in range(4):
+        q.copy_(torch.randn(q.shape, generator=torch.Generator().manual_seed(30 + rep)).to(torch.bfloat16))
+        k_new.copy_(torch.randn(k_new.shape, generator=torch.Generator().manual_seed(40 + rep)).to(torch.bfloat16))
+        v_new.copy_(torch.randn(v_new.shape, generator=torch.Generator().manual_seed(50 + rep)).to(torch.bfloat16))
+        ln = np.minimum(lens, rng.integers(1, lens + 1)).astype(np.int32)
+        fill(ln)
+        kc_ref, vc_ref = kc.clone(), vc.clone()
+        ref = torch.empty_like(out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(kc_ref, vc_ref, ref)          # the same step, eagerly
+        torch.cuda.synchronize()
+        # the oracle: each sequence's token scattered at position len - 1
+        # through its table, then decode by definition
+        pos = ln.astype(np.int64) - 1
+        slots = ora["decode_table"][np.arange(S), pos // 16].astype(np.int64) * 16 + pos % 16
+        paged.scatter(ok, to_numpy_storage(k_new), slots)
+        paged.scatter(ov, to_numpy_storage(v_new), slots)
+        assert to_numpy_storage(kc).tobytes() == ok.tobytes(), rep
+        assert to_numpy_storage(vc).tobytes() == ov.tobytes(), rep
+        want = paged.decode(to_numpy_storage(q), ok, ov, ora["decode_table"], ln, w.scale)
+        assert_close(out, want, "bf16", "append graph replay %d" % rep)
+        # the eager step wrote the same rows again: same pools, same output
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        assert torch.equal(kc.view(torch.int16), kc_ref.view(torch.int16)), rep
+        assert torch.equal(vc.view(torch.int16), vc_ref.view(torch.int16)), rep
