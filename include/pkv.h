@@ -491,11 +491,12 @@ int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_head
  * ["(2) vLLM Internals ...", 1.2 "Three Direct Wins", items 2 and 3;
  * "vLLM: what PagedAttention turned into", "The block pool, and the two
  * tricks in it"]). Same result as pkv_paged_attention_decode (to rounding),
- * computed as: every query against the shared prefix at once, as dense MFMA
- * tiles over all sequences' query rows (the prefix is read once per KV head
- * instead of once per sequence), then each sequence's own blocks, and a
- * merge that folds the prefix's softmax states with the sequence's own
- * (online-softmax rescaling, prefix first). The prefix block ids are read
+ * computed as: the queries against the shared prefix as dense MFMA tiles
+ * whose columns are the query rows of 8 to 32 sequences at once (the prefix
+ * is read once per KV head and column block instead of once per sequence),
+ * in the same launch as, and beside, the decode over each sequence's own
+ * blocks; then a merge that folds the prefix's softmax states with the
+ * sequence's own (online-softmax rescaling, prefix first). The prefix block ids are read
  * from row 0 of block_table; every sequence's context_lens must be at least
  * prefix_blocks*16 and its first prefix_blocks table entries equal row 0's
  * (caller contract; otherwise the result is undefined but every access stays

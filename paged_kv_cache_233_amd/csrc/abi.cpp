@@ -302,7 +302,7 @@ static SharedLayout shared_prefix_layout(int32_t num_seqs, int32_t num_q_heads,
   l.decode = (pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) + 255) /
              256 * 256;
   l.whole = ((size_t)num_seqs * num_q_heads * (head_dim + 4) * 4 + 255) / 256 * 256;
-  l.parts = pkv::prefix_state_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks * 16);
+  l.parts = pkv::decode_prefix_parts(num_seqs, num_q_heads, num_kv_heads, prefix_blocks);
   l.state = (size_t)l.parts * num_seqs * num_q_heads * (head_dim + 4) * 4;
   l.total = l.decode + l.whole + l.state;
   return l;
@@ -359,17 +359,12 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
   char* ws = reinterpret_cast<char*>(workspace);
   float* whole = reinterpret_cast<float*>(ws + l.decode);
   float* state = reinterpret_cast<float*>(ws + l.decode + l.whole);
-  pkv::PrefillArgs pa{nullptr, q, nullptr, nullptr, block_table, k_cache, v_cache, 1, num_seqs,
-                      num_blocks, max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads,
-                      head_dim, scale, dtype};
   pkv::DecodeArgs a{out, q, k_cache, v_cache, block_table, context_lens, num_seqs, num_blocks,
                     max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                     workspace};
-  const hipStream_t st = (hipStream_t)stream;
-  hipError_t err = pkv::launch_prefix_state(pa, prefix_blocks * 16, l.parts, state, st);
-  if (err != hipSuccess) return pkv::hip_fail(err, "shared-prefix phase launch");
-  err = pkv::launch_decode_after_prefix(a, prefix_blocks, state, l.parts, 3, st, whole);
-  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "decode launch");
+  const hipError_t err = pkv::launch_decode_shared_prefix(a, prefix_blocks, state, l.parts,
+                                                          (hipStream_t)stream, whole);
+  return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "shared-prefix decode launch");
 }
 
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,

@@ -68,19 +68,25 @@ struct DecodeParams {
   int32_t pieces_per_round;  // pieces whose query rows fit the LDS budget
   int32_t piece_cost;        // partition units a sequence costs besides its blocks
   float scale_log2;
-  // Shared-prefix mode: every sequence's first `skip` blocks were attended
-  // by the prefix phase, whose `pparts` softmax states per query row
+  // Shared-prefix mode: every sequence's first `skip` blocks (the same
+  // blocks in every row of the table) are attended once for all sequences,
+  // by `pwaves` extra workgroups after the decode waves (see prefix_wave).
+  // They leave `pparts` softmax states per query row
   // (pstate[part * pstride + row * (D + 4)]: O[D], max (log2 units), sum, two
-  // floats of padding that keep every row 16-byte aligned) the merge kernel
-  // folds before the sequence's own states. The split kernel then writes no
-  // output: it leaves the state of a sequence one wave holds whole in
-  // ws_whole[s * num_kv_heads + g] (G x (D + 4) floats), and the merge kernel
-  // writes every output. skip = 0 and pstate = nullptr otherwise.
+  // floats of padding that keep every row 16-byte aligned), which the merge
+  // kernel folds before the sequence's own states. The decode waves then
+  // write no output: they leave the state of a sequence one wave holds whole
+  // in ws_whole[s * num_kv_heads + g] (G x (D + 4) floats), and the merge
+  // kernel writes every output. skip = 0, pwaves = 0 and pstate = nullptr
+  // otherwise.
   int32_t skip;
   int32_t pparts;
-  const float* pstate;
+  float* pstate;
   int64_t pstride;
   float* ws_whole;
+  int32_t pwaves;    // prefix workgroups (a multiple of 8)
+  int32_t pcols;     // prefix column blocks per KV head
+  int32_t punits;    // num_kv_heads * pcols * pparts
   // Append mode (k_new != nullptr): before attending, the wave holding the
   // block of a sequence's last position writes that position's key and
   // value (k_new/v_new rows new_stride bytes apart, [num_kv_heads][D] each)
@@ -389,6 +395,245 @@ __device__ void merge_with_prefix(const DecodeParams& p, int32_t s, int32_t g, i
   }
 }
 
+// Query column blocks of a prefix wave: kPrefixNG groups of 16 MFMA columns
+// (16 / G sequences x the G query heads of one KV head each).
+constexpr int kPrefixNG = 2;
+// Bytes between K rows in a prefix wave's LDS tiles: 32 bytes of padding
+// keep the operand reads of 16 rows off shared banks.
+constexpr int kPrefixPad = 32;
+
+// LDS of a prefix wave: two K tiles.
+template <int D>
+constexpr size_t prefix_lds_bytes() {
+  return (size_t)2 * 16 * (D * 2 + kPrefixPad);
+}
+
+// A prefix tile in registers, K and V alike in the row-major layout of the
+// V operand of tile_attn.h: lane (n, kg) holds bytes [n*R/16, (n+1)*R/16)
+// of rows 4kg .. 4kg+3, so each load instruction reads 4 whole rows. (The
+// K operand layout, 16 rows x 64 bytes per instruction, takes the vector
+// memory pipeline about four times as long per byte; the K rows therefore
+// go to the MFMA layout through LDS.)
+template <int D>
+struct PrefixTile {
+  static constexpr int W = Shape<PKV_BF16, D>::kVWords;
+  uint32_t k[4][W];
+  uint32_t v[4][W];
+};
+
+template <int D>
+__device__ __forceinline__ void prefix_load(PrefixTile<D>& t, const char* kb, const char* vb,
+                                            uint32_t off) {
+  constexpr int R = Shape<PKV_BF16, D>::kRow;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_words<PrefixTile<D>::W, false>(t.k[j], kb + off + j * R);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_words<PrefixTile<D>::W, false>(t.v[j], vb + off + j * R);
+}
+
+// K rows of a tile into LDS (row r at r * pitch).
+template <int D>
+__device__ __forceinline__ void prefix_store_k(char* kl, const PrefixTile<D>& t, int n, int kg) {
+  constexpr int R = Shape<PKV_BF16, D>::kRow;
+  constexpr int pitch = R + kPrefixPad;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    char* dst = kl + (4 * kg + j) * pitch + n * (R / 16);
+    if constexpr (PrefixTile<D>::W == 4)
+      *reinterpret_cast<uint4*>(dst) = uint4{t.k[j][0], t.k[j][1], t.k[j][2], t.k[j][3]};
+    else
+      *reinterpret_cast<uint2*>(dst) = uint2{t.k[j][0], t.k[j][1]};
+  }
+}
+
+// Scores of one prefix tile for NG column groups: S = K Q^T, in the C
+// layout of the 16x16 MFMAs (as in tile_attn.h), the K operand read from
+// the LDS tile.
+template <int D, int NG>
+__device__ __forceinline__ void prefix_scores(f32x4 (&s)[NG], const char* kl,
+                                              const QOp<PKV_BF16, D> (&qv)[NG], int n, int kg) {
+  using Sh = Shape<PKV_BF16, D>;
+  constexpr int pitch = Sh::kRow + kPrefixPad;
+  uint4 ka[Sh::kKLoads];
+#pragma unroll
+  for (int c = 0; c < Sh::kKLoads; ++c)
+    ka[c] = *reinterpret_cast<const uint4*>(kl + n * pitch + 64 * c + 16 * kg);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    s[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < Sh::kKLoads; ++c)
+      s[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[c]),
+                                                      __builtin_bit_cast(bf16x8, qv[gi].c[c]), s[gi],
+                                                      0, 0, 0);
+  }
+}
+
+// Softmax step of one prefix tile (all 16 positions valid) and its PV
+// product. The weights are taken against a reference max per column that
+// moves only when a score passes it by more than 2^8 (log2 units: 8), so
+// the common step needs no cross-lane reduction: each lane keeps its own
+// partial sum (st.l), reduced over the column's four lanes at the end, and
+// the weights stay below 2^8. Any reference gives the same softmax once the
+// sum divides it out.
+template <int D, int NG>
+__device__ __forceinline__ void prefix_softmax_pv(State<PKV_BF16, D> (&st)[NG], const f32x4 (&s)[NG],
+                                                  const PrefixTile<D>& tl, float scale_log2) {
+  using Sh = Shape<PKV_BF16, D>;
+  float x[NG][4], lmax[NG];
+  bool move = false;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[gi][i] = s[gi][i] * scale_log2;
+    lmax[gi] = fmaxf(fmaxf(x[gi][0], x[gi][1]), fmaxf(x[gi][2], x[gi][3]));
+    move = move || lmax[gi] > st[gi].m + 8.0f;
+  }
+  if (__ballot(move) != 0) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float m_new = fmaxf(st[gi].m, wave_max_kg(lmax[gi]));
+      const float alpha = __builtin_amdgcn_exp2f(st[gi].m - m_new);
+      st[gi].l *= alpha;
+#pragma unroll
+      for (int e = 0; e < Sh::kTiles; ++e) st[gi].o[e] *= alpha;
+      st[gi].m = m_new;
+    }
+  }
+  i16x4 b[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = bf16_round(__builtin_amdgcn_exp2f(x[gi][i] - st[gi].m));
+    st[gi].l += (p[0] + p[1]) + (p[2] + p[3]);
+    bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]};
+    bf16x2 p23 = {(__bf16)p[2], (__bf16)p[3]};
+    uint2 pb = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+    b[gi] = __builtin_bit_cast(i16x4, pb);
+  }
+#pragma unroll
+  for (int e = 0; e < Sh::kTiles; ++e) {
+    // element e of each of the 4 rows this lane holds, packed as 4 bf16
+    const int w = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint2 a;
+    a.x = __builtin_amdgcn_perm(tl.v[1][w], tl.v[0][w], sel);
+    a.y = __builtin_amdgcn_perm(tl.v[3][w], tl.v[2][w], sel);
+    const i16x4 av = __builtin_bit_cast(i16x4, a);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+      st[gi].o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, b[gi], st[gi].o[e], 0, 0, 0);
+  }
+}
+
+// Shared-prefix mode: the prefix attention of one work unit (KV head g,
+// column block c, part k of the prefix blocks), run by workgroup
+// num_waves + pj of the split kernel beside the decode waves. The prefix
+// blocks are the first `skip` entries of row 0 of the table (every row holds
+// the same ones); part k covers blocks [k * skip / pparts, (k + 1) * skip /
+// pparts), at least one. The wave attends them for all its columns at once
+// and writes each query row's softmax state to the part's slice of pstate.
+// Per tile: the K rows, loaded a step earlier, go through LDS into the MFMA
+// layout; two tiles are in flight. Units are numbered head first and dealt
+// to the XCDs in contiguous eighths, like the decode waves, so one XCD's L2
+// serves the prefix blocks of its heads; prefix tiles are read by many
+// waves: cached loads.
+template <int D>
+__device__ __forceinline__ void prefix_wave(const DecodeParams& p, int32_t pj, char* lds) {
+  using Sh = Shape<PKV_BF16, D>;
+  constexpr int NG = kPrefixNG;
+  constexpr int pitch = Sh::kRow + kPrefixPad;
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  const int32_t per_xcd = p.pwaves / kXcds;
+  const int32_t unit = (pj % kXcds) * per_xcd + pj / kXcds;
+  if (unit >= p.punits) return;
+  const int32_t part = unit % p.pparts;
+  const int32_t gc = unit / p.pparts;
+  const int32_t c = gc % p.pcols;
+  const int32_t g = gc / p.pcols;
+  const int32_t G = p.group;
+  const int32_t tpg = 16 / G;                       // sequences per 16 columns
+  const int32_t b0 = (int32_t)((int64_t)part * p.skip / p.pparts);
+  const int32_t nt = (int32_t)((int64_t)(part + 1) * p.skip / p.pparts) - b0;
+  // column n of group gi: sequence (c * NG + gi) * tpg + n / G, head n % G
+  const int32_t ts = n / G;
+  const int32_t h = n - ts * G;
+  QOp<PKV_BF16, D> qv[NG];
+  State<PKV_BF16, D> st[NG];
+  int64_t row[NG];
+  bool valid[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int32_t sq = (c * NG + gi) * tpg + ts;
+    valid[gi] = ts < tpg && sq < p.num_seqs;
+    row[gi] = (int64_t)sq * p.num_q_heads + (int64_t)g * G + h;
+    load_query<PKV_BF16, D>(qv[gi], reinterpret_cast<const char*>(p.q) + row[gi] * Sh::kRow,
+                            valid[gi], kg);
+    st[gi].reset();
+  }
+  const uint32_t off = v_lane_offset<PKV_BF16, D>(n, kg);
+  char* kl[2] = {lds, lds + 16 * pitch};
+  // The part's tiles in chunks of up to 64: the chunk's block ids in a
+  // register (lane t: tile t of the chunk), read out per tile; tiles past
+  // the chunk's end repeat its last tile (loaded, never used). The tile
+  // loads are the only memory loads of the loop, so the compiler's wait
+  // counts stay exact.
+  for (int32_t cb = 0; cb < nt; cb += 64) {
+    const int32_t cn = min(64, nt - cb);
+    const int32_t ids = lane < cn ? p.block_table[b0 + cb + lane] : 0;
+    auto load = [&](PrefixTile<D>& t, int32_t k) {
+      int32_t id = __builtin_amdgcn_readlane(ids, min(k, cn - 1));
+      id = (uint32_t)id < (uint32_t)p.num_blocks ? id : 0;
+      const int64_t tb = ((int64_t)id * p.num_kv_heads + g) * Sh::kTileBytes;
+      prefix_load<D>(t, p.k_cache + tb, p.v_cache + tb, off);
+    };
+    auto step = [&](const char* k_lds, const PrefixTile<D>& t) {
+      f32x4 sc[NG];
+      prefix_scores<D, NG>(sc, k_lds, qv, n, kg);
+      prefix_softmax_pv<D, NG>(st, sc, t, p.scale_log2);
+    };
+    PrefixTile<D> buf[2];
+    load(buf[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(buf[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    prefix_store_k<D>(kl[0], buf[0], n, kg);
+    int32_t kb = 0;
+    for (; kb + 2 <= cn; kb += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // tile kb + u: K rows in kl[u], V rows in buf[u]
+        step(kl[u], buf[u]);
+        load(buf[u], kb + u + 2);
+        prefix_store_k<D>(kl[1 - u], buf[1 - u], n, kg);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (kb < cn) step(kl[0], buf[0]);
+  }
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float l = wave_sum_kg(st[gi].l);
+    if (!valid[gi]) continue;
+    float* o = p.pstate + part * p.pstride + row[gi] * (D + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = (4 * kg + i) * Sh::kTiles;
+#pragma unroll
+      for (int e = 0; e < Sh::kTiles; e += 4)
+        *reinterpret_cast<float4*>(o + d0 + e) =
+            float4{st[gi].o[e][i], st[gi].o[e + 1][i], st[gi].o[e + 2][i], st[gi].o[e + 3][i]};
+    }
+    if (kg == 0) {
+      o[D] = st[gi].m;
+      o[D + 1] = l;
+    }
+  }
+}
+
 // Piece of a wave's range: the tiles of one (sequence, KV head) it covers in
 // one round. Kept in LDS while the round streams.
 struct Piece {
@@ -426,10 +671,14 @@ decode_split_kernel(DecodeParams p) {
   Piece* pieces = reinterpret_cast<Piece*>(tile_head + kTilesPerRound);   // [kPiecesPerRound]
   int32_t* tails = reinterpret_cast<int32_t*>(pieces + kPiecesPerRound);  // [kPiecesPerRound]
   char* qlds = reinterpret_cast<char*>(tails + kPiecesPerRound);          // [kq][G * kRow]
+  const int32_t hw = blockIdx.x;
+  if (hw >= p.num_waves) {   // shared-prefix mode: a prefix workgroup
+    if constexpr (DT == PKV_BF16) prefix_wave<D>(p, hw - p.num_waves, lds);
+    return;
+  }
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int kg = lane >> 4;
-  const int32_t hw = blockIdx.x;
   const int32_t per_xcd = p.num_waves / kXcds;
   const int32_t w = (hw % kXcds) * per_xcd + hw / kXcds;
   const int32_t G = p.group;
@@ -829,18 +1078,20 @@ size_t split_lds_bytes(const DecodeParams& prm) {
 
 template <int DT, int D>
 hipError_t launch(const DecodeParams& prm, int phases, hipStream_t stream) {
-  const size_t lds = split_lds_bytes<DT, D>(prm);
+  size_t lds = split_lds_bytes<DT, D>(prm);
+  if (prm.pwaves > 0) lds = std::max(lds, prefix_lds_bytes<D>());   // the prefix waves' query rows
   if (phases & 1) {
   // 512-byte rows (fp32, head_dim 128) only fit two tiles in flight.
   const int depth = Shape<DT, D>::kRow > 256 ? 2 : decode_depth();
+  const dim3 grid(prm.num_waves + prm.pwaves);
   if constexpr (Shape<DT, D>::kRow > 256) {
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), grid, dim3(64), lds, stream, prm);
   } else if (depth == 2)
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 2>), grid, dim3(64), lds, stream, prm);
   else if (depth == 8)
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 8>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 8>), grid, dim3(64), lds, stream, prm);
   else
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, 4>), dim3(prm.num_waves), dim3(64), lds, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, 4>), grid, dim3(64), lds, stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -929,7 +1180,10 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return prefix + partial;
 }
 
-static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const float* pstate,
+// Sequences of one prefix work unit: kPrefixNG groups of 16 / G.
+static int32_t prefix_unit_seqs(int32_t group) { return kPrefixNG * (16 / group); }
+
+static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, float* pstate,
                                      int32_t pparts, int phases, hipStream_t stream,
                                      float* whole_states = nullptr) {
   DecodeParams p;
@@ -938,6 +1192,15 @@ static hipError_t launch_decode_impl(const DecodeArgs& a, int32_t skip, const fl
   p.pparts = pparts;
   p.ws_whole = whole_states;
   p.pstride = (int64_t)a.num_seqs * a.num_q_heads * (a.head_dim + 4);
+  p.pwaves = 0;
+  p.pcols = 0;
+  p.punits = 0;
+  if (pstate != nullptr) {
+    const int32_t us = prefix_unit_seqs(a.num_q_heads / a.num_kv_heads);
+    p.pcols = (a.num_seqs + us - 1) / us;
+    p.punits = a.num_kv_heads * p.pcols * pparts;
+    p.pwaves = (p.punits + kXcds - 1) / kXcds * kXcds;
+  }
   p.k_new = reinterpret_cast<const char*>(a.k_new);
   p.v_new = reinterpret_cast<const char*>(a.v_new);
   p.new_stride = a.new_token_stride * (a.dtype == PKV_F32 ? 4 : 2);
@@ -977,10 +1240,31 @@ hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream) {
   return launch_decode_impl(a, 0, nullptr, 0, phases, stream);
 }
 
-hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
-                                      const float* prefix_state, int32_t parts, int phases,
-                                      hipStream_t stream, float* whole_states) {
-  return launch_decode_impl(a, skip_blocks, prefix_state, parts, phases, stream, whole_states);
+constexpr int kMaxPrefixParts = 16;
+
+int decode_prefix_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t prefix_blocks) {
+  // About two prefix waves for every three decode waves (two per CU beside
+  // the decode's three), each part at least one block. Every part is one
+  // more state for the merge to fold per query row.
+  const int32_t us = prefix_unit_seqs(num_q_heads / num_kv_heads);
+  const int64_t base = std::max<int64_t>((int64_t)((num_seqs + us - 1) / us) * num_kv_heads, 1);
+  const int64_t target = std::max(2 * (int64_t)decode_num_waves() / 3, (int64_t)1);
+  int64_t parts = (target + base - 1) / base;
+  if (const char* env = getenv("PKV_PREFIX_PARTS")) {  // tuning override
+    const int v = atoi(env);
+    if (v >= 1 && v <= kMaxPrefixParts) parts = v;
+  }
+  parts = std::min<int64_t>(parts, std::max(prefix_blocks, 1));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kMaxPrefixParts));
+}
+
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, int32_t skip_blocks,
+                                       float* prefix_state, int32_t parts, hipStream_t stream,
+                                       float* whole_states) {
+  if (skip_blocks < 1 || parts < 1 || parts > skip_blocks || a.dtype != PKV_BF16)
+    return hipErrorInvalidValue;
+  return launch_decode_impl(a, skip_blocks, prefix_state, parts, 3, stream, whole_states);
 }
 
 }  // namespace pkv

@@ -68,14 +68,21 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num
 hipError_t decode_scratch(void** out);
 // phases: 1 = split-KV kernel, 2 = merge kernel, 3 = both.
 hipError_t launch_decode(const DecodeArgs& a, int phases, hipStream_t stream);
-// Decode over each sequence's blocks from `skip_blocks` on, the merge kernel
-// folding the `parts` prefix states (see launch_prefix_state) before each
-// sequence's own states. whole_states: num_seqs x num_kv_heads states of
-// G x (head_dim + 4) floats, where the split kernel leaves the state of a
-// sequence whose blocks one wave holds whole.
-hipError_t launch_decode_after_prefix(const DecodeArgs& a, int32_t skip_blocks,
-                                      const float* prefix_state, int32_t parts, int phases,
-                                      hipStream_t stream, float* whole_states);
+// Shared-prefix decode (bf16): one split-KV launch whose extra workgroups
+// attend the first `skip_blocks` blocks of table row 0 (common to every
+// sequence) in `parts` position ranges for all sequences at once, leaving
+// prefix_state[part][row][head_dim + 4] (unnormalised O, max in log2 units,
+// sum, two floats of padding; row = sequence * num_q_heads + head), while
+// its decode waves attend each sequence's blocks from skip_blocks on; then
+// the merge kernel folds the prefix states and the sequence's own states.
+// whole_states: num_seqs x num_kv_heads states of G x (head_dim + 4)
+// floats, where the split kernel leaves the state of a sequence whose
+// blocks one wave holds whole. 1 <= parts <= skip_blocks.
+int decode_prefix_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t prefix_blocks);
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, int32_t skip_blocks,
+                                       float* prefix_state, int32_t parts, hipStream_t stream,
+                                       float* whole_states);
 
 struct PrefillArgs {
   void* out;
