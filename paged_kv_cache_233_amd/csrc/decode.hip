@@ -402,91 +402,100 @@ constexpr int kPrefixNG = 2;
 // keep the operand reads of 16 rows off shared banks.
 constexpr int kPrefixPad = 32;
 
-// LDS of a prefix wave: two K tiles.
+// LDS of a prefix wave: the K rows of two pairs of tiles.
 template <int D>
 constexpr size_t prefix_lds_bytes() {
-  return (size_t)2 * 16 * (D * 2 + kPrefixPad);
+  return (size_t)4 * 16 * (D * 2 + kPrefixPad);
 }
 
-// A prefix tile in registers, K and V alike in the row-major layout of the
-// V operand of tile_attn.h: lane (n, kg) holds bytes [n*R/16, (n+1)*R/16)
-// of rows 4kg .. 4kg+3, so each load instruction reads 4 whole rows. (The
-// K operand layout, 16 rows x 64 bytes per instruction, takes the vector
-// memory pipeline about four times as long per byte; the K rows therefore
-// go to the MFMA layout through LDS.)
+// A pair of prefix tiles (32 positions) in registers, K and V alike in the
+// row-major layout of the V operand of tile_attn.h: lane (n, kg) holds
+// bytes [n*R/16, (n+1)*R/16) of rows 4kg .. 4kg+3 of each tile, so each
+// load instruction reads 4 whole rows. (The K operand layout, 16 rows x 64
+// bytes per instruction, takes the vector memory pipeline about four times
+// as long per byte, so the K rows go to the MFMA layout through LDS.)
 template <int D>
-struct PrefixTile {
+struct PrefixPair {
   static constexpr int W = Shape<PKV_BF16, D>::kVWords;
-  uint32_t k[4][W];
-  uint32_t v[4][W];
+  uint32_t k[2][4][W];
+  uint32_t v[2][4][W];
 };
 
 template <int D>
-__device__ __forceinline__ void prefix_load(PrefixTile<D>& t, const char* kb, const char* vb,
-                                            uint32_t off) {
+__device__ __forceinline__ void prefix_load(PrefixPair<D>& t, int h, const char* kb,
+                                            const char* vb, uint32_t off) {
   constexpr int R = Shape<PKV_BF16, D>::kRow;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_words<PrefixTile<D>::W, false>(t.k[j], kb + off + j * R);
+  for (int j = 0; j < 4; ++j) load_words<PrefixPair<D>::W, false>(t.k[h][j], kb + off + j * R);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_words<PrefixTile<D>::W, false>(t.v[j], vb + off + j * R);
+  for (int j = 0; j < 4; ++j) load_words<PrefixPair<D>::W, false>(t.v[h][j], vb + off + j * R);
 }
 
-// K rows of a tile into LDS (row r at r * pitch).
+// K rows of a pair into LDS (row r of tile h at (16h + r) * pitch).
 template <int D>
-__device__ __forceinline__ void prefix_store_k(char* kl, const PrefixTile<D>& t, int n, int kg) {
+__device__ __forceinline__ void prefix_store_k(char* kl, const PrefixPair<D>& t, int n, int kg) {
   constexpr int R = Shape<PKV_BF16, D>::kRow;
   constexpr int pitch = R + kPrefixPad;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    char* dst = kl + (4 * kg + j) * pitch + n * (R / 16);
-    if constexpr (PrefixTile<D>::W == 4)
-      *reinterpret_cast<uint4*>(dst) = uint4{t.k[j][0], t.k[j][1], t.k[j][2], t.k[j][3]};
-    else
-      *reinterpret_cast<uint2*>(dst) = uint2{t.k[j][0], t.k[j][1]};
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      char* dst = kl + (16 * h + 4 * kg + j) * pitch + n * (R / 16);
+      if constexpr (PrefixPair<D>::W == 4)
+        *reinterpret_cast<uint4*>(dst) = uint4{t.k[h][j][0], t.k[h][j][1], t.k[h][j][2], t.k[h][j][3]};
+      else
+        *reinterpret_cast<uint2*>(dst) = uint2{t.k[h][j][0], t.k[h][j][1]};
+    }
 }
 
-// Scores of one prefix tile for NG column groups: S = K Q^T, in the C
-// layout of the 16x16 MFMAs (as in tile_attn.h), the K operand read from
-// the LDS tile.
+// One step of a prefix wave over a pair of tiles (32 positions; the second
+// tile's positions are dropped when `both` is false) for NG column groups:
+//   scores S = K Q^T (16x16x32 MFMAs, the K operand read from the LDS rows);
+//   weights against a reference max per column that moves only when a score
+//     passes it by more than 2^8 (log2 units: 8), so the common step needs
+//     no cross-lane reduction: each lane keeps its own partial sum (st.l),
+//     reduced over the column's four lanes at the end, and the weights stay
+//     below 2^8 (any reference gives the same softmax once the sum divides
+//     it out);
+//   O^T += V^T P^T over all 32 positions in one 16x16x32 MFMA per output
+//     tile: lane (n, kg) holds the weights of rows 4kg..4kg+3 of both tiles
+//     (the C layout of the score MFMAs), which is the B layout when the
+//     contraction index runs over tile 0's four rows, then tile 1's, in each
+//     group of eight; the V operand packs the same rows' values.
 template <int D, int NG>
-__device__ __forceinline__ void prefix_scores(f32x4 (&s)[NG], const char* kl,
-                                              const QOp<PKV_BF16, D> (&qv)[NG], int n, int kg) {
+__device__ __forceinline__ void prefix_step(State<PKV_BF16, D> (&st)[NG], const char* kl,
+                                            const PrefixPair<D>& t, const QOp<PKV_BF16, D> (&qv)[NG],
+                                            float scale_log2, bool both, int n, int kg) {
   using Sh = Shape<PKV_BF16, D>;
   constexpr int pitch = Sh::kRow + kPrefixPad;
-  uint4 ka[Sh::kKLoads];
+  f32x4 s[2][NG];
 #pragma unroll
-  for (int c = 0; c < Sh::kKLoads; ++c)
-    ka[c] = *reinterpret_cast<const uint4*>(kl + n * pitch + 64 * c + 16 * kg);
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    s[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < 2; ++h) {
+    uint4 ka[Sh::kKLoads];
 #pragma unroll
     for (int c = 0; c < Sh::kKLoads; ++c)
-      s[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[c]),
-                                                      __builtin_bit_cast(bf16x8, qv[gi].c[c]), s[gi],
-                                                      0, 0, 0);
+      ka[c] = *reinterpret_cast<const uint4*>(kl + (16 * h + n) * pitch + 64 * c + 16 * kg);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      s[h][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < Sh::kKLoads; ++c)
+        s[h][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[c]),
+                                                           __builtin_bit_cast(bf16x8, qv[gi].c[c]),
+                                                           s[h][gi], 0, 0, 0);
+    }
   }
-}
-
-// Softmax step of one prefix tile (all 16 positions valid) and its PV
-// product. The weights are taken against a reference max per column that
-// moves only when a score passes it by more than 2^8 (log2 units: 8), so
-// the common step needs no cross-lane reduction: each lane keeps its own
-// partial sum (st.l), reduced over the column's four lanes at the end, and
-// the weights stay below 2^8. Any reference gives the same softmax once the
-// sum divides it out.
-template <int D, int NG>
-__device__ __forceinline__ void prefix_softmax_pv(State<PKV_BF16, D> (&st)[NG], const f32x4 (&s)[NG],
-                                                  const PrefixTile<D>& tl, float scale_log2) {
-  using Sh = Shape<PKV_BF16, D>;
-  float x[NG][4], lmax[NG];
+  float x[NG][8], lmax[NG];
   bool move = false;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[gi][i] = s[gi][i] * scale_log2;
-    lmax[gi] = fmaxf(fmaxf(x[gi][0], x[gi][1]), fmaxf(x[gi][2], x[gi][3]));
+    for (int i = 0; i < 4; ++i) {
+      x[gi][i] = s[0][gi][i] * scale_log2;
+      x[gi][4 + i] = both ? s[1][gi][i] * scale_log2 : -INFINITY;
+    }
+    lmax[gi] = fmaxf(fmaxf(fmaxf(x[gi][0], x[gi][1]), fmaxf(x[gi][2], x[gi][3])),
+                     fmaxf(fmaxf(x[gi][4], x[gi][5]), fmaxf(x[gi][6], x[gi][7])));
     move = move || lmax[gi] > st[gi].m + 8.0f;
   }
   if (__ballot(move) != 0) {
@@ -500,30 +509,30 @@ __device__ __forceinline__ void prefix_softmax_pv(State<PKV_BF16, D> (&st)[NG], 
       st[gi].m = m_new;
     }
   }
-  i16x4 b[NG];
+  bf16x8 b[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    float p[4];
+    float p[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = bf16_round(__builtin_amdgcn_exp2f(x[gi][i] - st[gi].m));
-    st[gi].l += (p[0] + p[1]) + (p[2] + p[3]);
-    bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]};
-    bf16x2 p23 = {(__bf16)p[2], (__bf16)p[3]};
-    uint2 pb = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-    b[gi] = __builtin_bit_cast(i16x4, pb);
+    for (int i = 0; i < 8; ++i) p[i] = bf16_round(__builtin_amdgcn_exp2f(x[gi][i] - st[gi].m));
+    st[gi].l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[gi][i] = (__bf16)p[i];
   }
 #pragma unroll
   for (int e = 0; e < Sh::kTiles; ++e) {
-    // element e of each of the 4 rows this lane holds, packed as 4 bf16
+    // element e of each of the 4 rows this lane holds of each tile
     const int w = e >> 1;
     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint2 a;
-    a.x = __builtin_amdgcn_perm(tl.v[1][w], tl.v[0][w], sel);
-    a.y = __builtin_amdgcn_perm(tl.v[3][w], tl.v[2][w], sel);
-    const i16x4 av = __builtin_bit_cast(i16x4, a);
+    uint4 a;
+    a.x = __builtin_amdgcn_perm(t.v[0][1][w], t.v[0][0][w], sel);
+    a.y = __builtin_amdgcn_perm(t.v[0][3][w], t.v[0][2][w], sel);
+    a.z = __builtin_amdgcn_perm(t.v[1][1][w], t.v[1][0][w], sel);
+    a.w = __builtin_amdgcn_perm(t.v[1][3][w], t.v[1][2][w], sel);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi)
-      st[gi].o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, b[gi], st[gi].o[e], 0, 0, 0);
+      st[gi].o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[gi], st[gi].o[e], 0, 0, 0);
   }
 }
 
@@ -532,13 +541,13 @@ __device__ __forceinline__ void prefix_softmax_pv(State<PKV_BF16, D> (&st)[NG], 
 // num_waves + pj of the split kernel beside the decode waves. The prefix
 // blocks are the first `skip` entries of row 0 of the table (every row holds
 // the same ones); part k covers blocks [k * skip / pparts, (k + 1) * skip /
-// pparts), at least one. The wave attends them for all its columns at once
-// and writes each query row's softmax state to the part's slice of pstate.
-// Per tile: the K rows, loaded a step earlier, go through LDS into the MFMA
-// layout; two tiles are in flight. Units are numbered head first and dealt
-// to the XCDs in contiguous eighths, like the decode waves, so one XCD's L2
-// serves the prefix blocks of its heads; prefix tiles are read by many
-// waves: cached loads.
+// pparts), at least one. The wave attends them for all its columns at once,
+// a pair of tiles per step, and writes each query row's softmax state to the
+// part's slice of pstate. The K rows of a pair, loaded a step earlier, go
+// through LDS into the MFMA layout; two pairs are in flight. Units are
+// numbered head first and dealt to the XCDs in contiguous eighths, like the
+// decode waves, so one XCD's L2 serves the prefix blocks of its heads;
+// prefix tiles are read by many waves: cached loads.
 template <int D>
 __device__ __forceinline__ void prefix_wave(const DecodeParams& p, int32_t pj, char* lds) {
   using Sh = Shape<PKV_BF16, D>;
@@ -575,7 +584,7 @@ __device__ __forceinline__ void prefix_wave(const DecodeParams& p, int32_t pj, c
     st[gi].reset();
   }
   const uint32_t off = v_lane_offset<PKV_BF16, D>(n, kg);
-  char* kl[2] = {lds, lds + 16 * pitch};
+  char* kl[2] = {lds, lds + 32 * pitch};
   // The part's tiles in chunks of up to 64: the chunk's block ids in a
   // register (lane t: tile t of the chunk), read out per tile; tiles past
   // the chunk's end repeat its last tile (loaded, never used). The tile
@@ -583,36 +592,35 @@ __device__ __forceinline__ void prefix_wave(const DecodeParams& p, int32_t pj, c
   // counts stay exact.
   for (int32_t cb = 0; cb < nt; cb += 64) {
     const int32_t cn = min(64, nt - cb);
+    const int32_t np = (cn + 1) >> 1;               // pairs of the chunk
     const int32_t ids = lane < cn ? p.block_table[b0 + cb + lane] : 0;
-    auto load = [&](PrefixTile<D>& t, int32_t k) {
-      int32_t id = __builtin_amdgcn_readlane(ids, min(k, cn - 1));
-      id = (uint32_t)id < (uint32_t)p.num_blocks ? id : 0;
-      const int64_t tb = ((int64_t)id * p.num_kv_heads + g) * Sh::kTileBytes;
-      prefix_load<D>(t, p.k_cache + tb, p.v_cache + tb, off);
+    auto load = [&](PrefixPair<D>& t, int32_t q) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        int32_t id = __builtin_amdgcn_readlane(ids, min(2 * q + hh, cn - 1));
+        id = (uint32_t)id < (uint32_t)p.num_blocks ? id : 0;
+        const int64_t tb = ((int64_t)id * p.num_kv_heads + g) * Sh::kTileBytes;
+        prefix_load<D>(t, hh, p.k_cache + tb, p.v_cache + tb, off);
+      }
     };
-    auto step = [&](const char* k_lds, const PrefixTile<D>& t) {
-      f32x4 sc[NG];
-      prefix_scores<D, NG>(sc, k_lds, qv, n, kg);
-      prefix_softmax_pv<D, NG>(st, sc, t, p.scale_log2);
-    };
-    PrefixTile<D> buf[2];
+    PrefixPair<D> buf[2];
     load(buf[0], 0);
     __builtin_amdgcn_sched_barrier(0);
     load(buf[1], 1);
     __builtin_amdgcn_sched_barrier(0);
     prefix_store_k<D>(kl[0], buf[0], n, kg);
-    int32_t kb = 0;
-    for (; kb + 2 <= cn; kb += 2) {
+    int32_t q = 0;
+    for (; q + 2 <= np; q += 2) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        // tile kb + u: K rows in kl[u], V rows in buf[u]
-        step(kl[u], buf[u]);
-        load(buf[u], kb + u + 2);
+        // pair q + u: K rows in kl[u], V rows in buf[u]
+        prefix_step<D, NG>(st, kl[u], buf[u], qv, p.scale_log2, 2 * (q + u) + 1 < cn, n, kg);
         prefix_store_k<D>(kl[1 - u], buf[1 - u], n, kg);
+        load(buf[u], q + u + 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kb < cn) step(kl[0], buf[0]);
+    if (q < np) prefix_step<D, NG>(st, kl[0], buf[0], qv, p.scale_log2, 2 * q + 1 < cn, n, kg);
   }
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
@@ -1244,12 +1252,15 @@ constexpr int kMaxPrefixParts = 16;
 
 int decode_prefix_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t prefix_blocks) {
-  // About two prefix waves for every three decode waves (two per CU beside
+  // About one prefix wave for every three decode waves (one per CU beside
   // the decode's three), each part at least one block. Every part is one
-  // more state for the merge to fold per query row.
+  // more state for the merge to fold per query row. (The prefix waves' L2
+  // reads slow the decode waves beside them, whatever their number: on 128
+  // sequences sharing a 2048-token prefix the whole call takes 44.5 us with
+  // 2 parts, 45.2 with 4, 51.2 with 8.)
   const int32_t us = prefix_unit_seqs(num_q_heads / num_kv_heads);
   const int64_t base = std::max<int64_t>((int64_t)((num_seqs + us - 1) / us) * num_kv_heads, 1);
-  const int64_t target = std::max(2 * (int64_t)decode_num_waves() / 3, (int64_t)1);
+  const int64_t target = std::max((int64_t)decode_num_waves() / 3, (int64_t)1);
   int64_t parts = (target + base - 1) / base;
   if (const char* env = getenv("PKV_PREFIX_PARTS")) {  // tuning override
     const int v = atoi(env);

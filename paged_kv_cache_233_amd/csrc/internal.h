@@ -106,14 +106,4 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Shared-prefix decode, first phase: the softmax states of every query
-// (total_q sequences' tokens) over positions [0, prefix_tokens) of
-// block_table row 0, split in `parts` position ranges; state[part][row][D+4]
-// holds unnormalised O, the reference max (log2 units), the sum and two
-// floats of padding (16-byte aligned rows). bf16 only.
-int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t prefix_tokens);
-hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int32_t parts,
-                               float* state, hipStream_t stream);
-
 }  // namespace pkv

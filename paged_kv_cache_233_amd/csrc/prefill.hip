@@ -58,16 +58,6 @@ struct PrefillParams {
   int32_t group;          // query heads per KV head
   int32_t tokens_per_group;  // query tokens per 16-column group = 16 / group
   float scale_log2;
-  // Shared-prefix mode (bf16 LDS kernel only): cu_q_lens == nullptr means
-  // one group of total_q query tokens that all see positions
-  // [0, fixed_ctx) of block_table row 0 (no causal mask); the softmax states
-  // (unnormalised O, reference max in log2 units, sum) are written to
-  // state[part][row][D + 4] instead of out, the positions being split in
-  // `parts` contiguous ranges over as many workgroups.
-  int32_t fixed_ctx;
-  int32_t parts;
-  float* state;
-  int64_t state_part_stride;   // floats per part
 };
 
 template <int DT, int D, int NG, int DEPTH>
@@ -479,11 +469,9 @@ prefill_lds_kernel(LdsParams lp) {
   const int32_t wg = (hw & 7) * lp.per_xcd + (hw >> 3);
   if (wg >= lp.num_wg) return;
   const int32_t rb = wg % lp.row_blocks;
-  const int32_t part = (wg / lp.row_blocks) % p.parts;
-  const int32_t pair = wg / lp.row_blocks / p.parts;
+  const int32_t pair = wg / lp.row_blocks;
   const int32_t g = pair % p.num_kv_heads;
   const int32_t ch = pair / p.num_kv_heads;
-  const bool direct = p.cu_q_lens == nullptr;   // shared-prefix mode
 
   const int tid = threadIdx.x;
   // (wave-uniform values are made visibly uniform, so that the decisions
@@ -499,14 +487,12 @@ prefill_lds_kernel(LdsParams lp) {
   lds_char* s_ids = lds + half * kIds * 4;
   lds_char* bufs = lds + kRoundIds * 4 + half * kBufs * L::kBuf;
 
-  const int32_t q_begin = direct ? 0 : max(0, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch]));
-  const int32_t q_end = direct ? p.total_q
-                               : min(p.total_q, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch + 1]));
+  const int32_t q_begin = max(0, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch]));
+  const int32_t q_end = min(p.total_q, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch + 1]));
   const int32_t qlen = max(0, min(q_end - q_begin, p.max_q_len));
-  int32_t ctx = direct ? p.fixed_ctx : __builtin_amdgcn_readfirstlane(p.context_lens[ch]);
+  int32_t ctx = __builtin_amdgcn_readfirstlane(p.context_lens[ch]);
   ctx = max(0, min(ctx, p.max_blocks * 16));
-  // direct mode: every query sits past the context, seeing all of it
-  const int32_t p0 = direct ? ctx : max(ctx - qlen, 0);
+  const int32_t p0 = max(ctx - qlen, 0);
   const int32_t wg_tok0 = rb * (kWaves * NG * tpg);
   if (wg_tok0 >= qlen) return;  // whole workgroup idle: before any barrier
   const int32_t wg_tok_last = min(wg_tok0 + kWaves * NG * tpg, qlen) - 1;
@@ -530,25 +516,7 @@ prefill_lds_kernel(LdsParams lp) {
                             valid[gi], kg);
   }
 
-  const int32_t ntiles_all = lim_wg / kKeys + 1;
-  const int32_t per_part = (ntiles_all + p.parts - 1) / p.parts;
-  const int32_t t_lo = part * per_part;
-  const int32_t t_hi = min(t_lo + per_part, ntiles_all);
-  if (p.state != nullptr && (lim_wg < 0 || t_lo >= t_hi)) {
-    // Nothing to attend to in this part: an empty state (weight 0 later).
-    if (half != 0) return;
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      if (!valid[gi]) continue;
-      float* st = p.state + part * p.state_part_stride + row[gi] * (D + 4);
-      for (int d = 4 * kg; d < D; d += 16) *reinterpret_cast<float4*>(st + d) = float4{0.f, 0.f, 0.f, 0.f};
-      if (kg == 0) {
-        st[D] = kNoMax;
-        st[D + 1] = 0.f;
-      }
-    }
-    return;
-  }
+  const int32_t ntiles = lim_wg / kKeys + 1;
   if (lim_wg < 0) {
     // Empty context: nothing to attend to, zero output.
     if (half != 0) return;
@@ -578,12 +546,12 @@ prefill_lds_kernel(LdsParams lp) {
   const float c = p.scale_log2;
   const float tau_raw = kLazyMax / c;
   const int32_t nblk = lim_wg / 16 + 1;        // blocks any row of this workgroup sees
-  // Tiles of this half: [tbeg, tbeg + tcnt) within the part's [t_lo, t_hi).
-  // The first half has the most tiles; both halves take the same number of
-  // steps, the second one's surplus steps being fully masked.
-  const int32_t steps = (t_hi - t_lo + SPLIT - 1) / SPLIT;
-  const int32_t tbeg = t_lo + half * steps;
-  const int32_t tcnt = max(0, min(steps, t_hi - tbeg));
+  // Tiles of this half: [tbeg, tbeg + tcnt) of [0, ntiles). The first half
+  // has the most tiles; both halves take the same number of steps, the
+  // second one's surplus steps being fully masked.
+  const int32_t steps = (ntiles + SPLIT - 1) / SPLIT;
+  const int32_t tbeg = half * steps;
+  const int32_t tcnt = max(0, min(steps, ntiles - tbeg));
   const int32_t* trow = p.block_table + (int64_t)ch * p.max_blocks;
   const uint32_t block_stride = (uint32_t)p.num_kv_heads * L::kRow * 16;
   const char* kbase = p.k_cache + (int64_t)g * L::kRow * 16;
@@ -676,24 +644,6 @@ prefill_lds_kernel(LdsParams lp) {
     }
   }
 
-  if (p.state != nullptr) {
-    // Shared-prefix mode: the state itself, dims in natural order.
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      if (!valid[gi]) continue;
-      float* st = p.state + part * p.state_part_stride + row[gi] * (D + 4);
-#pragma unroll
-      for (int e = 0; e < kE; ++e)
-        *reinterpret_cast<float4*>(st + 16 * e + 4 * kg) =
-            float4{acc.o[gi][e][0], acc.o[gi][e][1], acc.o[gi][e][2], acc.o[gi][e][3]};
-      if (kg == 0) {
-        st[D] = acc.mc[gi];
-        st[D + 1] = acc.l[gi][0];
-      }
-    }
-    return;
-  }
-
   // Lane (n, kg) writes dims 16e + 4kg + 0..3 of its column's row.
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
@@ -759,7 +709,7 @@ hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream) {
   lp.p = prm;
   const int32_t wg_tokens = kWaves * NG * prm.tokens_per_group;
   lp.row_blocks = (prm.max_q_len + wg_tokens - 1) / wg_tokens;
-  const int64_t nwg = (int64_t)lp.row_blocks * prm.num_kv_heads * prm.num_chunks * prm.parts;
+  const int64_t nwg = (int64_t)lp.row_blocks * prm.num_kv_heads * prm.num_chunks;
   if (nwg * 64 * kWaves * 2 > INT32_MAX) return hipErrorInvalidConfiguration;
   lp.num_wg = (int32_t)nwg;
   lp.per_xcd = (lp.num_wg + 7) / 8;
@@ -817,65 +767,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.group = a.num_q_heads / a.num_kv_heads;
   p.tokens_per_group = 16 / p.group;
   p.scale_log2 = a.scale * kLog2e;
-  p.fixed_ctx = 0;
-  p.parts = 1;
-  p.state = nullptr;
-  p.state_part_stride = 0;
   if (a.dtype == PKV_BF16)
     return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, stream) : launch<PKV_BF16, 64>(p, stream);
   return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream) : launch<PKV_F32, 64>(p, stream);
-}
-
-constexpr int kMaxPrefixParts = 16;
-
-int prefix_state_parts(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t prefix_tokens) {
-  // About one workgroup per two CUs: (row blocks x KV heads) x parts, each
-  // part keeping at least two 32-position tiles. With fewer workgroups than
-  // two per CU each runs eight waves over two halves of its positions. Every
-  // part is one more state for the merge to fold per query row, and past
-  // about half the CUs the extra parallelism no longer pays for it (the whole
-  // shared-prefix decode of 128 sequences over a 2048-token prefix: 2 parts
-  // 57.1 us, 4 parts 51.8, 8 parts 52.1).
-  const int32_t group = num_q_heads / num_kv_heads;
-  const int32_t wg_tokens = kWaves * 2 * (16 / group);
-  const int64_t base = (int64_t)((num_seqs + wg_tokens - 1) / wg_tokens) * num_kv_heads;
-  const int32_t tiles = (prefix_tokens + kKeys - 1) / kKeys;
-  int64_t parts = ((int64_t)num_cus() + 2 * base - 1) / (2 * base);
-  parts = std::min<int64_t>(parts, std::max<int32_t>(1, tiles / 2));
-  if (const char* env = getenv("PKV_PREFIX_PARTS")) {  // tuning override
-    const int v = atoi(env);
-    if (v >= 1 && v <= kMaxPrefixParts) parts = v;
-  }
-  return (int)std::max<int64_t>(1, std::min<int64_t>(parts, kMaxPrefixParts));
-}
-
-hipError_t launch_prefix_state(const PrefillArgs& a, int32_t prefix_tokens, int32_t parts,
-                               float* state, hipStream_t stream) {
-  PrefillParams p;
-  p.out = nullptr;
-  p.q = a.q;
-  p.cu_q_lens = nullptr;
-  p.context_lens = nullptr;
-  p.block_table = a.block_table;
-  p.k_cache = reinterpret_cast<const char*>(a.k_cache);
-  p.v_cache = reinterpret_cast<const char*>(a.v_cache);
-  p.num_chunks = 1;
-  p.total_q = a.total_q;
-  p.num_blocks = a.num_blocks;
-  p.max_blocks = a.max_blocks_per_seq;
-  p.max_q_len = a.total_q;
-  p.num_q_heads = a.num_q_heads;
-  p.num_kv_heads = a.num_kv_heads;
-  p.group = a.num_q_heads / a.num_kv_heads;
-  p.tokens_per_group = 16 / p.group;
-  p.scale_log2 = a.scale * kLog2e;
-  p.fixed_ctx = prefix_tokens;
-  p.parts = parts;
-  p.state = state;
-  p.state_part_stride = (int64_t)a.total_q * a.num_q_heads * (a.head_dim + 4);
-  if (a.dtype != PKV_BF16) return hipErrorInvalidValue;
-  return a.head_dim == 128 ? launch_lds<128, 2>(p, stream) : launch_lds<64, 2>(p, stream);
 }
 
 }  // namespace pkv

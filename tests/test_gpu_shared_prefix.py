@@ -123,9 +123,9 @@ def test_shared_prefix_full_shared_workload_sampled():
 @pytest.mark.parametrize("parts", [1, 2, 5, 16])
 def test_shared_prefix_any_number_of_prefix_parts(parts):
     """The prefix positions cut into 1 to 16 parts, whose softmax states the
-    decode folds at each sequence's first piece: every count matches the
-    oracle, for sequences with a suffix of their own and for one whose
-    context ends with the prefix."""
+    merge folds before each sequence's own: every count matches the oracle,
+    for sequences with a suffix of their own and for one whose context ends
+    with the prefix."""
     print("[gpu] shared prefix, %d parts" % parts, flush=True)
     prefix = 1024
     w = workloads.custom("spp", 71, [prefix + x for x in (1, 1, 17, 300, 2, 64)], shared_prefix=prefix,
@@ -151,3 +151,31 @@ def test_shared_prefix_any_number_of_prefix_parts(parts):
     qs = to_numpy_storage(q)
     ref = paged.decode(qs, ora["k_cache"], ora["v_cache"], ora["decode_table"], lens_np, w.scale)
     assert_close(out, ref, "bf16", "parts %d" % parts)
+
+
+@pytest.mark.parametrize("name", ["bf16 d128 group 4", "bf16 d64 group 8"])
+def test_shared_prefix_part_longer_than_64_blocks(name):
+    """One part holding all 66 prefix blocks: its block ids are read 64 at a
+    time, so the part runs as two chunks, the second of two tiles (one pair)
+    and, with 67 blocks, of three (a pair and a single tile)."""
+    for prefix_blocks in (66, 67):
+        prefix = 16 * prefix_blocks
+        print("[gpu] shared prefix %s, %d blocks in one part" % (name, prefix_blocks), flush=True)
+        w = workloads.custom("spl", 74, [prefix + x for x in (3, 40, 16, 200, 1)],
+                             shared_prefix=prefix, **CASES[name])
+        nat = run_native(w, prefill=False)
+        q, table, lens = _inputs(w, nat)
+        out = torch.empty_like(q)
+        old = os.environ.get("PKV_PREFIX_PARTS")
+        os.environ["PKV_PREFIX_PARTS"] = "1"
+        try:
+            pkv.decode_shared_prefix(out, q, nat["k_cache"], nat["v_cache"], table, lens,
+                                     prefix_blocks, w.scale)
+            torch.cuda.synchronize()
+        finally:
+            if old is None:
+                del os.environ["PKV_PREFIX_PARTS"]
+            else:
+                os.environ["PKV_PREFIX_PARTS"] = old
+        ora = run_oracle(w, prefill=False)
+        assert_close(out, ora["decode"], "bf16", "%s, %d blocks" % (name, prefix_blocks))
