@@ -179,3 +179,46 @@ def test_shared_prefix_part_longer_than_64_blocks(name):
                 os.environ["PKV_PREFIX_PARTS"] = old
         ora = run_oracle(w, prefill=False)
         assert_close(out, ora["decode"], "bf16", "%s, %d blocks" % (name, prefix_blocks))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_shared_prefix_random_shapes(seed):
+    """Seeded random shapes: group size, KV heads, head_dim, batch size,
+    prefix length (1 to 80 blocks), suffix lengths, some sequences holding
+    the prefix alone, and the number of prefix parts."""
+    rng = np.random.default_rng(5000 + seed)
+    group = [1, 2, 3, 4, 8, 16][int(rng.integers(6))]
+    hkv = [1, 2, 4, 8][int(rng.integers(4))]
+    d = [64, 128][int(rng.integers(2))]
+    n = int(rng.integers(1, 41))
+    pb = int(rng.integers(1, 81))
+    prefix = 16 * pb
+    suffix = [int(rng.integers(1, 300)) for _ in range(n)]
+    parts = [None, 1, 2, 3, 7, 16][int(rng.integers(6))]
+    print("[gpu] shared prefix random %d: G=%d hkv=%d d=%d seqs=%d prefix blocks=%d parts=%s"
+          % (seed, group, hkv, d, n, pb, parts), flush=True)
+    w = workloads.custom("spr%d" % seed, 6000 + seed, [prefix + x for x in suffix],
+                         shared_prefix=prefix, num_q_heads=hkv * group, num_kv_heads=hkv,
+                         head_dim=d, dtype="bf16")
+    nat = run_native(w, prefill=False)
+    q, table, _ = _inputs(w, nat)
+    lens_np = nat["decode_lens"].copy()
+    for i in np.nonzero(rng.random(n) < 0.2)[0]:
+        lens_np[i] = prefix                 # the prefix alone
+    lens = torch.from_numpy(lens_np).cuda()
+    out = torch.empty_like(q)
+    old = os.environ.get("PKV_PREFIX_PARTS")
+    if parts is not None:
+        os.environ["PKV_PREFIX_PARTS"] = str(parts)
+    try:
+        pkv.decode_shared_prefix(out, q, nat["k_cache"], nat["v_cache"], table, lens, pb, w.scale)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("PKV_PREFIX_PARTS", None)
+        else:
+            os.environ["PKV_PREFIX_PARTS"] = old
+    ora = run_oracle(w, prefill=False)
+    ref = paged.decode(to_numpy_storage(q), ora["k_cache"], ora["v_cache"], ora["decode_table"],
+                       lens_np, w.scale)
+    assert_close(out, ref, "bf16", "shared prefix random %d" % seed)
