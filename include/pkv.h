@@ -492,7 +492,7 @@ int pkv_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_head
  * "vLLM: what PagedAttention turned into", "The block pool, and the two
  * tricks in it"]). Same result as pkv_paged_attention_decode (to rounding),
  * computed as: the queries against the shared prefix as dense MFMA tiles
- * whose columns are the query rows of 8 to 32 sequences at once (the prefix
+ * whose columns are the query rows of 2 to 32 sequences at once (the prefix
  * is read once per KV head and column block instead of once per sequence),
  * in the same launch as, and beside, the decode over each sequence's own
  * blocks; then a merge that folds the prefix's softmax states with the
