@@ -247,6 +247,37 @@ class HipEvents:
             raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
         return ms.value * 1e3
 
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+    def burst_us(self, stream, launch, reps, bursts=5, prime=2):
+        """Per-call time of `launch(i)`, the median over `bursts` bursts of
+        `reps` calls, each burst between its own pair of events. A burst
+        starts on an idle device with `prime` untimed calls queued ahead of
+        its first event, so the device never waits on the host inside it. The
+        events time the device, idle gaps included: a host stall of tens of
+        milliseconds (the process descheduled) spoils the one burst it falls
+        in, and the median drops that burst."""
+        import statistics
+
+        import torch
+
+        per_call = []
+        for _ in range(bursts):
+            torch.cuda.synchronize()
+            for i in range(prime):
+                launch(i)
+            e0, e1 = self.create(), self.create()
+            self.record(e0, stream)
+            for i in range(reps):
+                launch(prime + i)
+            self.record(e1, stream)
+            self.sync(e1)
+            per_call.append(self.elapsed_us(e0, e1) / reps)
+            self.destroy(e0)
+            self.destroy(e1)
+        return statistics.median(per_call)
+
 
 def kernel_source_hash(srcs=None):
     h = hashlib.sha256()
@@ -800,7 +831,8 @@ def shared_leg(args, dev):
     128 physical blocks) decoded two ways: the ordinary decode (every
     sequence reads the prefix through its table) and the shared-prefix
     decode (the prefix attended once for all sequences as MFMA tiles, then
-    each sequence's own blocks). Reports kernel time and GB/s on logical
+    each sequence's own blocks). Reports kernel time (median of five timed
+    bursts) and GB/s on logical
     bytes (every attended token's K/V once per sequence) and on unique bytes
     (each physical block once)."""
     import numpy as np
@@ -837,13 +869,7 @@ def shared_leg(args, dev):
     def timed(fn):
         for r in range(5):
             fn(*pools[r % len(pools)])
-        e0, e1 = hip.create(), hip.create()
-        hip.record(e0, sh)
-        for r in range(reps):
-            fn(*pools[r % len(pools)])
-        hip.record(e1, sh)
-        torch.cuda.synchronize()
-        return hip.elapsed_us(e0, e1) / reps
+        return hip.burst_us(sh, lambda i: fn(*pools[i % len(pools)]), reps)
 
     plain = timed(lambda kc, vc: pkv.decode(out, q, kc, vc, d_table, d_lens, w.scale, ws))
     shared = timed(lambda kc, vc: pkv.decode_shared_prefix(out, q, kc, vc, d_table, d_lens,
@@ -865,8 +891,8 @@ def shared_leg(args, dev):
 
 def prefill_leg(args, dev):
     """Chunked prefill on the mixed workload's two 512-query chunks (cached
-    prefixes of the seeded lengths), all K/V resident: kernel time, tokens/s
-    and MFMA throughput on the algorithmic FLOPs (unmasked query-key pairs
+    prefixes of the seeded lengths), all K/V resident: kernel time (median of
+    five timed bursts), tokens/s and MFMA throughput on the algorithmic FLOPs (unmasked query-key pairs
     only: 4 * head_dim * query heads per pair)."""
     import numpy as np
     import torch
@@ -899,13 +925,8 @@ def prefill_leg(args, dev):
     reps = max(10, args.steps // 2)
     hip = HipEvents()
     sh = torch.cuda.current_stream().cuda_stream
-    e0, e1 = hip.create(), hip.create()
-    hip.record(e0, sh)
-    for _ in range(reps):
-        pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax, w.scale)
-    hip.record(e1, sh)
-    torch.cuda.synchronize()
-    us = hip.elapsed_us(e0, e1) / reps
+    us = hip.burst_us(sh, lambda i: pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax,
+                                                      w.scale), reps)
     pairs = 0
     for spec in ch:
         # queries at positions cached .. total-1 see position+1 keys each
