@@ -174,3 +174,48 @@ def test_prefill_index_arrays_in_pinned_host_memory():
                       nat["k_cache"], nat["v_cache"], int(max(s.new_tokens for s in w.chunk_seqs)), w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), nat["prefill"].view(torch.int16))
+
+
+def _check_rows_one_by_one(w, nat, what, rows=8):
+    """The first and last `rows` query rows of every chunk against the
+    oracle, each set computed as a chunk of its own (a query's result depends
+    only on its position and the tokens before it) on the oracle's own pools
+    and allocator table."""
+    from oracle import paged
+
+    ora = run_oracle(w, prefill=False)
+    sids = [s.seq_id for s in w.chunk_seqs]
+    table, lens = ora["model"].block_table(sids, w.max_blocks_per_seq())
+    assert np.array_equal(table, nat["prefill_table"]) and np.array_equal(lens, nat["prefill_lens"])
+    cu = nat["prefill_cu"]
+    q = to_numpy_storage(torch.cat([w.seq_q(s) for s in w.chunk_seqs]))
+    for c in range(len(sids)):
+        lo, hi, n = int(cu[c]), int(cu[c + 1]), int(lens[c])
+        for a, b, ctx in ((lo, lo + rows, n - (hi - lo) + rows), (hi - rows, hi, n)):
+            ref = paged.prefill_chunk(q[a:b], [0, b - a], [ctx], ora["k_cache"], ora["v_cache"],
+                                      table[c:c + 1], w.scale)
+            assert_close(nat["prefill"][a:b], ref, w.dtype, "%s chunk %d rows %d..%d" % (what, c, a, b))
+
+
+def test_prefill_context_beyond_one_round_two_halves():
+    """Contexts past 32768 positions, so that a workgroup stages its block
+    ids in more than one round (1024 tiles of 32 positions per round and
+    tile half): 64 queries over 40000 cached tokens and 200 over 33000, few
+    enough row blocks that each workgroup splits its tiles over two sets of
+    waves. Sampled rows against the oracle."""
+    w = workloads.custom("pfr2", 60, [], chunks=[(40000, 64), (33000, 200)], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, dtype="bf16")
+    _announce("prefill past one round, two tile halves")
+    nat = run_native(w)
+    _check_rows_one_by_one(w, nat, "two halves")
+
+
+def test_prefill_context_beyond_one_round_one_set_of_waves():
+    """The same past 32768 positions with enough row blocks (4 chunks of 512
+    queries: 512 workgroups) that each workgroup walks all its tiles with
+    one set of waves."""
+    w = workloads.custom("pfr1", 61, [], chunks=[(33500, 512)] * 4, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, dtype="bf16")
+    _announce("prefill past one round, one set of waves")
+    nat = run_native(w)
+    _check_rows_one_by_one(w, nat, "one set")
