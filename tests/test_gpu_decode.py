@@ -536,3 +536,29 @@ def test_decode_thousands_of_short_sequences():
     _check_tables(nat, ora)
     assert to_numpy_storage(nat["k_cache"]).tobytes() == ora["k_cache"].tobytes()
     assert_close(nat["decode"], ora["decode"], "bf16", "2000 short")
+
+
+def test_decode_rounds_cut_by_the_tile_limit():
+    """One wave per CU over 3 sequences of about 131072 tokens and 8 KV heads:
+    every wave's range holds more tiles than one round's 512, so rounds are
+    cut by the tile limit inside a sequence and the next round continues the
+    open piece. Plain and append mode, both against the oracle (outputs and,
+    in append mode, the whole pools)."""
+    w = workloads.custom("rounds", 37, [131072, 131072, 131000], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    _announce("decode rounds cut by the tile limit (one wave per CU)")
+    try:
+        pkv.decode_set_waves_per_cu(1)
+        nat = run_native(w, prefill=False)
+        nat_app = run_native(w, prefill=False, fused_append=True)
+    finally:
+        pkv.decode_set_waves_per_cu(0)
+    waves = (torch.cuda.get_device_properties(0).multi_processor_count + 7) // 8 * 8
+    per_wave = sum((s.total + 15) // 16 for s in w.decode_seqs) * w.num_kv_heads / waves
+    assert per_wave > 512, per_wave
+    ora = run_oracle(w, prefill=False)
+    _check_tables(nat, ora)
+    assert_close(nat["decode"], ora["decode"], "bf16", "tile-limit rounds")
+    assert to_numpy_storage(nat_app["k_cache"]).tobytes() == ora["k_cache"].tobytes()
+    assert to_numpy_storage(nat_app["v_cache"]).tobytes() == ora["v_cache"].tobytes()
+    assert torch.equal(nat_app["decode"].view(torch.int16), nat["decode"].view(torch.int16))
