@@ -13,11 +13,11 @@
 // bf16 (prefill_lds_kernel): a workgroup of 4 waves owns 4*NG column groups
 // of one (chunk, KV head) and walks that sequence's K/V in tiles of 32
 // positions (two pool blocks). The four waves load each tile once, together,
-// into LDS (three buffers: one being filled while one is scored and one is
-// multiplied), and every wave reads its MFMA operands from there, so the
-// tile crosses from L2 once per workgroup instead of once per wave. Both
-// products run on the 16x16x32 bf16 MFMA. The softmax keeps a lazily
-// updated running max: a row's reference max moves only when a score
+// straight from global memory into LDS (two buffers: the next tile lands in
+// one while the other is read), and every wave reads its MFMA operands from
+// there, so the tile crosses from L2 once per workgroup instead of once per
+// wave. Both products run on the 16x16x32 bf16 MFMA. The softmax keeps a
+// lazily updated running max: a row's reference max moves only when a score
 // exceeds it by more than 2^8, so the rescale of the accumulators (which
 // would otherwise follow almost every tile) is skipped; the result is the
 // same softmax, since any reference value cancels in the normalisation.
@@ -172,7 +172,6 @@ prefill_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------ bf16, LDS
 constexpr int kKeys = 32;          // positions per LDS tile (two pool blocks)
-constexpr int kBufs = 2;           // LDS tile buffers per tile pipeline
 constexpr int kRoundIds = 2048;    // block ids staged in LDS per round
 constexpr float kLazyMax = 8.0f;   // log2 of the largest weight before a rescale
 constexpr float kNoMax = -1e30f;   // reference max of a row that has seen nothing
@@ -181,30 +180,32 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-// LDS tile layout. K and V rows are padded by 32 bytes (8 words), which
-// keeps the column-wise K operand reads and the transposing V reads (four
-// rows of 32 bytes per 16 lanes) off shared banks: the bank-conflict
-// counter reads zero for the whole kernel. (K rows padded by 16 bytes, a
-// layout made for 32 banks, spent 24% of the LDS's active cycles in bank
-// conflicts on gfx950.)
+// LDS tile layout. A tile's K rows (32 positions of one head, 2*D bytes
+// each) and then its V rows, unpadded; the 16-byte chunks of row r sit at
+// chunk index c ^ swz(r). The swizzle spreads both operand reads over the
+// 64 banks: the K operand read (16 rows x 64 bytes per instruction) finds
+// four rows in each 64-byte bank window, the transposing V read (16 rows x
+// 32 bytes) two rows in each 32-byte window.
 template <int D>
 struct Lds {
   static constexpr int kRow = 2 * D;                  // bytes of one position of one head
-  static constexpr int kPitchK = kRow + 32;
-  static constexpr int kPitchV = kRow + 32;
-  static constexpr int kPieces = kRow / 16;           // 16-byte pieces per row
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kPerThread = kKeys * kPieces / kThreads;
-  static constexpr int kBlockPieces = 16 * kPieces;   // pieces of one (block, head) tile
-  static constexpr int kHalfK = kKeys * kPitchK;      // K part of one buffer
-  static constexpr int kBuf = kHalfK + kKeys * kPitchV;
-  static_assert(kPerThread >= 1, "tile smaller than the workgroup");
-  static_assert(kBlockPieces % 64 == 0, "a wave's pieces must lie in one block");
+  static constexpr int kChunks = kRow / 16;           // 16-byte chunks per row
+  static constexpr int kTile = kKeys * kRow;          // one tensor's tile
+  static constexpr int kBuf = 2 * kTile;              // K tile, then V tile
+  static constexpr int kThreads = 64 * kWaves;        // threads of one tile pipeline
+  static constexpr int kRowsPerLoad = 1024 / kRow;    // rows one wave's 64 x 16-byte load fills
+  static constexpr int kLoads = kTile / (1024 * kWaves);  // loads per wave and tensor
+  static_assert(kLoads >= 1 && 16 % kRowsPerLoad == 0, "a load's rows must lie in one block");
 };
 
-// Calls f(std::integral_constant<int, 0>) ... f(<N-1>): the staged tile
-// registers are then indexed by constants from the start, which keeps them
-// in registers.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + 2 * ((r >> 2) & 1);
+  else return 2 * ((r >> 1) & 3);
+}
+
+// Calls f(std::integral_constant<int, 0>) ... f(<N-1>): the per-load values
+// are then indexed by constants, which keeps them in registers.
 template <typename F, int... I>
 __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -214,110 +215,100 @@ __device__ __forceinline__ void unroll(F&& f) {
   unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-// Native 4 x 32-bit vector: loads, stores and copies stay plain vector
-// operations (the HIP uint4 class copies through memcpy, which can leave the
-// staged tile in scratch memory).
+// Native 4 x 32-bit vector: loads and copies stay plain vector operations.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// One thread's share of a tile on its way from global memory to LDS.
-template <int D>
-struct Staged {
-  u32x4 k[Lds<D>::kPerThread];
-  u32x4 v[Lds<D>::kPerThread];
-};
+// Sixteen bytes of zeros per lane: the source of V rows past the
+// workgroup's last visible position (so that their zero weights cannot
+// meet a NaN in the pool).
+static __device__ __align__(16) const char kZeroRows[1024] = {};
 
-// Loop-invariant offsets of one thread. Piece u of the thread is 16 bytes of
-// tile position srow[u]; all pieces of one wave lie in the same pool block
-// (blk[u], wave-uniform), so the block's address is scalar arithmetic and
-// the load takes a scalar base plus this 32-bit offset.
+// Loop-invariant offsets of one thread. Load u of the thread's wave fills
+// LDS bytes [1024 * (wq * kLoads + u), +1024) of a tensor's tile, lane l the
+// 16 bytes at +16 l: row srow[u], chunk l % kChunks, which holds the
+// source chunk (l % kChunks) ^ swz(row). All rows of one load lie in one
+// pool block (blk[u], wave-uniform), so the block's address is scalar and
+// the load takes it plus this 32-bit offset.
 template <int D>
 struct Lanes {
-  uint32_t gofs[Lds<D>::kPerThread];  // byte offset inside the (block, head) tile
-  uint32_t kst[Lds<D>::kPerThread];   // LDS byte offset of the K piece in a buffer
-  uint32_t vst[Lds<D>::kPerThread];   // LDS byte offset of the V piece in a buffer
-  int32_t srow[Lds<D>::kPerThread];   // tile position
-  int32_t blk[Lds<D>::kPerThread];    // which of the tile's two blocks
-  uint32_t kofs;                      // K operand read offset (lane (n, kg))
-  uint32_t vofs;                      // V operand read offset (lane (n, kg))
+  static constexpr int kC = Lds<D>::kRow / 64;  // 64-byte K operand reads per 16 rows
+  static constexpr int kE = D / 16;             // 16-dim V tiles
+  uint32_t gofs[Lds<D>::kLoads];  // source byte offset inside the (block, head) tile
+  uint32_t lofs[Lds<D>::kLoads];  // LDS byte offset of the load in a tensor tile (uniform)
+  int32_t srow[Lds<D>::kLoads];   // tile position of the lane's piece
+  int32_t blk[Lds<D>::kLoads];    // which of the tile's two blocks (uniform)
+  uint32_t kofs[kC];              // K operand read offsets (lane (n, kg), rows 0..15)
+  uint32_t vofs[kE];              // V operand read offsets (lane (n, kg), rows 4kg + n / 4)
 
-  __device__ __forceinline__ void init(int tid, int n, int kg) {
+  __device__ __forceinline__ void init(int wq, int lane, int n, int kg) {
     using L = Lds<D>;
-    unroll<L::kPerThread>([&](auto uc) {
+    unroll<L::kLoads>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      const int q = tid + L::kThreads * u;
-      const int r = q / L::kPieces;
-      const int col = 16 * (q % L::kPieces);
-      gofs[u] = (uint32_t)(q % L::kBlockPieces) * 16u;
-      kst[u] = (uint32_t)(r * L::kPitchK + col);
-      vst[u] = (uint32_t)(L::kHalfK + r * L::kPitchV + col);
+      const int r = (wq * L::kLoads + u) * L::kRowsPerLoad + lane / L::kChunks;
+      const int c = lane % L::kChunks;
+      gofs[u] = (uint32_t)((r % 16) * L::kRow + 16 * (c ^ swz<D>(r)));
+      lofs[u] = (uint32_t)((wq * L::kLoads + u) * 1024);
       srow[u] = r;
-      blk[u] = __builtin_amdgcn_readfirstlane(q / L::kBlockPieces);
+      blk[u] = (wq * L::kLoads + u) * L::kRowsPerLoad / 16;
     });
-    kofs = (uint32_t)(n * L::kPitchK + 16 * kg);
+    // K operand: lane (n, kg) reads 16 bytes (dims 8kg..8kg+7 of 64c..64c+31)
+    // of row n: chunk kg + 4c.
+#pragma unroll
+    for (int c = 0; c < kC; ++c) kofs[c] = (uint32_t)(n * L::kRow + 16 * ((kg + 4 * c) ^ swz<D>(n)));
     // Transposing V read: lane 4j + q of a 16-lane group reads 8 bytes (dims
-    // 4q..4q+3 of the tile's 16) of position 4kg + j; lane n then receives
-    // dim n of positions 4kg + 0..3.
-    vofs = (uint32_t)(L::kHalfK + (4 * kg + n / 4) * L::kPitchV + 8 * (n % 4));
+    // 4q..4q+3 of dim tile e) of row 4kg + j; lane n then receives dim n of
+    // rows 4kg + 0..3.
+    const int row = 4 * kg + n / 4, q = n % 4;
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+      vofs[e] = (uint32_t)(L::kTile + row * L::kRow + 16 * ((2 * e + (q >> 1)) ^ swz<D>(row)) +
+                           8 * (q & 1));
   }
 };
 
-// Global -> registers: this thread's pieces of tile `jl` of the round (ids
-// of its two blocks at s_ids[2*jl], [2*jl+1]).
+// Global -> LDS, directly: this wave's loads of tile `jl` of the round (ids
+// of its two blocks at s_ids[2*jl], [2*jl+1]) into buffer `buf`. V rows
+// past `vlim` load zeros. Completion is tracked by the wave's vector memory
+// counter; the buffer is read only after a wait and a barrier.
 template <int D>
-__device__ __forceinline__ void tile_fetch(Staged<D>& st, const Lanes<D>& ln, const char* kbase,
-                                           const char* vbase, uint32_t block_stride,
-                                           const lds_char* s_ids, int jl) {
-  unroll<Lds<D>::kPerThread>([&](auto uc) {
-    constexpr int u = decltype(uc)::value;
+__device__ __forceinline__ void stage_tile(const Lanes<D>& ln, lds_char* buf, const char* kbase,
+                                          const char* vbase, uint32_t block_stride,
+                                          const lds_char* s_ids, int jl, int t0, int vlim,
+                                          int lane) {
+  using L = Lds<D>;
+#pragma unroll
+  for (int u = 0; u < L::kLoads; ++u) {
     const int32_t id = *reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(
         s_ids + 4 * (2 * jl + ln.blk[u]));
     // 32 x 32 -> 64-bit product in scalar registers (block_stride < 2^32)
     const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(id);
     const uint64_t off = ((uint64_t)__umulhi(b, block_stride) << 32) | (uint32_t)(b * block_stride);
-    st.k[u] = *reinterpret_cast<const u32x4*>(kbase + off + ln.gofs[u]);
-    st.v[u] = *reinterpret_cast<const u32x4*>(vbase + off + ln.gofs[u]);
-  });
-}
-
-// Registers -> LDS buffer. V rows past `vlim` (no query of this workgroup
-// sees them; the pool may hold anything there) are stored as zeros, so that
-// their zero weights cannot meet a NaN.
-template <int D>
-__device__ __forceinline__ void tile_store(const Staged<D>& st, const Lanes<D>& ln, lds_char* buf,
-                                           int t0, int vlim) {
-  using L = Lds<D>;
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  if (t0 + kKeys - 1 <= vlim) {
-    unroll<L::kPerThread>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      *reinterpret_cast<lds_u32x4*>(buf + ln.kst[u]) = st.k[u];
-      *reinterpret_cast<lds_u32x4*>(buf + ln.vst[u]) = st.v[u];
-    });
-  } else {
-    unroll<L::kPerThread>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      const uint32_t keep = t0 + ln.srow[u] <= vlim ? ~0u : 0u;
-      *reinterpret_cast<lds_u32x4*>(buf + ln.kst[u]) = st.k[u];
-      *reinterpret_cast<lds_u32x4*>(buf + ln.vst[u]) = st.v[u] & keep;
-    });
+    const uint32_t lofs = (uint32_t)__builtin_amdgcn_readfirstlane(ln.lofs[u]);
+    const char* vsrc = t0 + ln.srow[u] <= vlim ? vbase + off + ln.gofs[u] : kZeroRows + 16 * lane;
+    // (the builtin exists only for the device target: the host pass, which
+    // never runs this, does not see it)
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(kbase + off + ln.gofs[u], (lds_void*)(buf + lofs), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(buf + L::kTile + lofs), 16, 0, 0);
+#endif
   }
 }
 
 // Scores of one LDS tile against NG column groups: s[gi][h] holds, in lane
 // (n, kg), S[16h + 4kg + i][n] (position offset within the tile, column n).
 template <int D, int NG>
-__device__ __forceinline__ void tile_scores(f32x4 (&s)[NG][2], const lds_char* buf, uint32_t kofs,
-                                            const QOp<PKV_BF16, D> (&qv)[NG]) {
+__device__ __forceinline__ void tile_scores(f32x4 (&s)[NG][2], const lds_char* buf,
+                                            const Lanes<D>& ln, const QOp<PKV_BF16, D> (&qv)[NG]) {
   using L = Lds<D>;
   typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
   constexpr int kC = L::kRow / 64;
-  const lds_char* base = buf + kofs;
   u32x4 kf[2][kC];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int c = 0; c < kC; ++c)
-      kf[h][c] = *reinterpret_cast<lds_u32x4*>(base + 16 * h * L::kPitchK + 64 * c);
+      kf[h][c] = *reinterpret_cast<lds_u32x4*>(buf + ln.kofs[c] + 16 * h * L::kRow);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
@@ -358,19 +349,19 @@ __device__ __forceinline__ float max8(const float (&x)[8]) {
 // per-column causal limit (tiles that reach past the wave's smallest limit).
 template <int D, int NG>
 __device__ __forceinline__ void tile_softmax_pv(const f32x4 (&s)[NG][2], const lds_char* buf,
-                                                uint32_t vofs, Acc<D, NG>& a,
+                                                const Lanes<D>& ln, Acc<D, NG>& a,
                                                 const int (&lim)[NG], int t0, bool mask, float c,
                                                 float tau_raw, int kg) {
   using L = Lds<D>;
   constexpr int kE = D / 16;
-  // V operands first: their LDS latency then overlaps the softmax.
-  const lds_char* vb = buf + vofs;
+  // V operands first: their LDS latency then overlaps the softmax. (Rows
+  // 16.. of the tile have the same swizzle as rows 0..15.)
   bf16x8 av[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 32 * e));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + ln.vofs[e]));
     const i16x4_t hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 16 * L::kPitchV + 32 * e));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + ln.vofs[e] + 16 * L::kRow));
     av[e] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
   float x[NG][8];
@@ -458,8 +449,14 @@ prefill_lds_kernel(LdsParams lp) {
   constexpr int kE = D / 16;
   constexpr int kIds = kRoundIds / SPLIT;     // block ids per half and round
   constexpr int kBigPos = 1 << 30;            // position of a tile past every limit
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  lds_char* lds = (lds_char*)smem;
+  constexpr int kPer = 2 + 4 * kE;            // floats of a lane's softmax state per group
+  // Two tile buffers per pipeline, as separate arrays: the compiler then
+  // sees that the loads filling one never touch the other, and lets this
+  // wave read one while its loads into the other are in flight.
+  __shared__ __attribute__((aligned(16))) char s_bufa[SPLIT][L::kBuf];
+  __shared__ __attribute__((aligned(16))) char s_bufb[SPLIT][L::kBuf];
+  __shared__ __attribute__((aligned(16))) int32_t s_idarr[kRoundIds];
+  __shared__ __attribute__((aligned(16))) float s_xs[SPLIT == 2 ? NG * kPer * 256 : 1];
   const PrefillParams& p = lp.p;
 
   // XCD-aware placement: hardware workgroup b runs on XCD b % 8; the
@@ -484,8 +481,9 @@ prefill_lds_kernel(LdsParams lp) {
   const int kg = lane >> 4;
   const int32_t G = p.group;
   const int32_t tpg = p.tokens_per_group;
-  lds_char* s_ids = lds + half * kIds * 4;
-  lds_char* bufs = lds + kRoundIds * 4 + half * kBufs * L::kBuf;
+  lds_char* s_ids = (lds_char*)s_idarr + half * kIds * 4;
+  lds_char* const bufa = (lds_char*)s_bufa[half];
+  lds_char* const bufb = (lds_char*)s_bufb[half];
 
   const int32_t q_begin = max(0, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch]));
   const int32_t q_end = min(p.total_q, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch + 1]));
@@ -557,7 +555,7 @@ prefill_lds_kernel(LdsParams lp) {
   const char* kbase = p.k_cache + (int64_t)g * L::kRow * 16;
   const char* vbase = p.v_cache + (int64_t)g * L::kRow * 16;
   Lanes<D> ln;
-  ln.init(htid, n, kg);
+  ln.init(wq, lane, n, kg);
 
   for (int32_t j0 = 0; j0 < steps; j0 += kIds / 2) {
     const int32_t nt = min(kIds / 2, steps - j0);    // steps of this round
@@ -572,44 +570,52 @@ prefill_lds_kernel(LdsParams lp) {
     __syncthreads();
     // Position of tile i of the round; a step with no tile of this half
     // gets a position past every limit (its K/V rows are block 0's, masked,
-    // and its V is stored as zeros).
+    // and its V rows load as zeros).
     auto pos = [&](int32_t i) -> int32_t {
       return i < nv ? kKeys * (tbeg + j0 + i) : kBigPos;
     };
-    // Step i: fetch tile i+1 from global memory, score tile i and take its
-    // softmax and PV product, store tile i+1 into the other buffer, which
-    // tile i-1 used. Near the round's end a step fetches the last tile again
-    // and stores it into the buffer no later step reads.
-    Staged<D> st;
-    tile_fetch<D>(st, ln, kbase, vbase, block_stride, s_ids, 0);
-    tile_store<D>(st, ln, bufs, pos(0), lim_wg);
+    // Step i: the loads of tile i+1 go into the other buffer (which tile
+    // i-1 used) while this wave scores tile i and takes its softmax and PV
+    // product; then each wave waits for its own loads and the barrier makes
+    // every wave's visible. Tiles alternate between the two buffers, which
+    // the loop names directly (a buffer chosen at run time would hide from
+    // the compiler that the in-flight loads never touch the buffer read).
+#define PKV_TILE_LOAD(buf, i)                                                              \
+  stage_tile<D>(ln, buf, kbase, vbase, block_stride, s_ids, i, pos(i), lim_wg, lane)
+#define PKV_TILE_ATTEND(buf, i)                                                            \
+  do {                                                                                     \
+    f32x4 sc[NG][2];                                                                       \
+    tile_scores<D, NG>(sc, buf, ln, qv);                                                   \
+    const int32_t t0 = pos(i);                                                             \
+    tile_softmax_pv<D, NG>(sc, buf, ln, acc, lim, t0, t0 + kKeys - 1 > lim_min, c, tau_raw, \
+                           kg);                                                            \
+  } while (0)
+    PKV_TILE_LOAD(bufa, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
-    uint32_t b0 = 0, b1 = L::kBuf;  // buffers of tiles i and i+1
-    for (int32_t i = 0; i < nt; ++i) {
-      const int32_t inext = min(i + 1, nt - 1);
-      tile_fetch<D>(st, ln, kbase, vbase, block_stride, s_ids, inext);
-      f32x4 sc[NG][2];
-      tile_scores<D, NG>(sc, bufs + b0, ln.kofs, qv);
-      const int32_t t0 = pos(i);
-      tile_softmax_pv<D, NG>(sc, bufs + b0, ln.vofs, acc, lim, t0, t0 + kKeys - 1 > lim_min, c,
-                             tau_raw, kg);
-      tile_store<D>(st, ln, bufs + b1, pos(inext), lim_wg);
+    int32_t i = 0;
+    for (; i + 2 <= nt; i += 2) {
+      PKV_TILE_LOAD(bufb, i + 1);
+      PKV_TILE_ATTEND(bufa, i);
+      __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();
-      const uint32_t t = b0;
-      b0 = b1;
-      b1 = t;
+      if (i + 2 < nt) PKV_TILE_LOAD(bufa, i + 2);
+      PKV_TILE_ATTEND(bufb, i + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
     }
+    if (i < nt) PKV_TILE_ATTEND(bufa, i);
+#undef PKV_TILE_LOAD
+#undef PKV_TILE_ATTEND
   }
 
   if constexpr (SPLIT == 2) {
     // Waves 4..7 hand (reference max, sum, accumulators) to the waves 0..3
     // that own the same rows, lane for lane; value v of lane t sits at float
     // v * 256 + t.
-    constexpr int kPer = 2 + 4 * kE;
     typedef __attribute__((address_space(3))) float lds_float;
-    lds_float* xs = (lds_float*)(lds + kRoundIds * 4);
-    static_assert(NG * kPer * 256 * 4 <= 2 * kBufs * Lds<D>::kBuf, "merge area too small");
-    __syncthreads();  // all tile reads done before the buffers are reused
+    lds_float* xs = (lds_float*)s_xs;
+    __syncthreads();
     if (half == 1) {
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
@@ -692,14 +698,9 @@ int num_cus() {
 
 template <int D, int NG, int SPLIT>
 hipError_t launch_lds_split(const LdsParams& lp, hipStream_t stream) {
-  const size_t lds = kRoundIds * 4 + SPLIT * kBufs * Lds<D>::kBuf;
-  auto kern = prefill_lds_kernel<D, NG, SPLIT>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(8 * lp.per_xcd), dim3(64 * kWaves * SPLIT), lds, stream, lp);
+  // (LDS: static arrays of the kernel)
+  hipLaunchKernelGGL((prefill_lds_kernel<D, NG, SPLIT>), dim3(8 * lp.per_xcd),
+                     dim3(64 * kWaves * SPLIT), 0, stream, lp);
   return hipGetLastError();
 }
 
@@ -715,11 +716,7 @@ hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream) {
   lp.per_xcd = (lp.num_wg + 7) / 8;
   // Two waves per SIMD either way: with fewer than two workgroups per CU,
   // each workgroup splits its tiles over two sets of waves.
-  // (The hand-over of the split needs its state to fit the tile buffers.)
-  constexpr bool kCanSplit = NG * (2 + 4 * (D / 16)) * 256 * 4 <= 2 * kBufs * Lds<D>::kBuf;
-  if constexpr (kCanSplit) {
-    if (nwg < 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 2>(lp, stream);
-  }
+  if (nwg < 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 2>(lp, stream);
   return launch_lds_split<D, NG, 1>(lp, stream);
 }
 
