@@ -84,7 +84,7 @@ def parse():
     ap.add_argument("--shared-probe", action="store_true",
                     help="only run the shared-prefix leg and print its JSON (for profiling it alone)")
     ap.add_argument("--prefill-probe", action="store_true",
-                    help="only run the chunked-prefill leg and print its JSON (for profiling it alone)")
+                    help="only run the chunked-prefill leg on the mixed chunks and print its JSON (for profiling it alone)")
     return ap.parse_args()
 
 
@@ -564,7 +564,7 @@ def main():
         print(json.dumps({"shared_prefix": shared_leg(args, dev)}), flush=True)
         return
     if args.prefill_probe:
-        print(json.dumps({"prefill": prefill_leg(args, dev)}), flush=True)
+        print(json.dumps({"prefill": prefill_leg(args, dev, long_context=False)}), flush=True)
         return
     w = workloads.named(args.config)
     hip = HipEvents()
@@ -889,7 +889,7 @@ def shared_leg(args, dev):
             "shared_prefix_unique_gbs": round(unique / shared / 1e3, 1)}
 
 
-def prefill_leg(args, dev):
+def prefill_leg(args, dev, long_context=True):
     """Chunked prefill on the mixed workload's two 512-query chunks (cached
     prefixes of the seeded lengths), all K/V resident: kernel time (median of
     five timed bursts), tokens/s and MFMA throughput on the algorithmic FLOPs (unmasked query-key pairs
@@ -925,8 +925,10 @@ def prefill_leg(args, dev):
     reps = max(10, args.steps // 2)
     hip = HipEvents()
     sh = torch.cuda.current_stream().cuda_stream
+    # (the library asks for no workspace here: 256 row blocks, one per CU)
+    pws = pkv.prefill_workspace(len(ch), w.num_q_heads, w.num_kv_heads, w.head_dim, qmax, dev)
     us = hip.burst_us(sh, lambda i: pkv.prefill_chunk(out, q, d_cu, d_lens, d_table, kc, vc, qmax,
-                                                      w.scale), reps)
+                                                      w.scale, pws), reps)
     pairs = 0
     for spec in ch:
         # queries at positions cached .. total-1 see position+1 keys each
@@ -942,7 +944,50 @@ def prefill_leg(args, dev):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "traffic": load_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SRCS,
-                                                 "prefill_source_sha256")}}
+                                                 "prefill_source_sha256")},
+            "long_context": prefill_long_context(args, dev) if long_context else None}
+
+
+def prefill_long_context(args, dev):
+    """One 512-query chunk over 30000 cached tokens (same heads): 128 row
+    blocks for 256 CUs, so with the workspace the library asks for each row
+    block's positions are cut into two parts (a second kernel folds them).
+    Kernel time with and without the workspace (median of five bursts)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_233_amd as pkv
+    import workloads
+
+    w = workloads.custom("prefill long", 11, [], chunks=[(30000, 512)], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, dtype="bf16")
+    ch = w.chunk_seqs
+    alloc, kc, vc = build_pool(w, dev, w.num_blocks, step=True)
+    table, lens = alloc.block_table([s.seq_id for s in ch], w.max_blocks_per_seq())
+    q = w.seq_q(ch[0]).to(dev)
+    out = torch.empty_like(q)
+    a = (torch.tensor([0, q.shape[0]], dtype=torch.int32, device=dev), torch.from_numpy(lens).to(dev),
+         torch.from_numpy(table).to(dev))
+    qmax = int(q.shape[0])
+    ws = pkv.prefill_workspace(1, w.num_q_heads, w.num_kv_heads, w.head_dim, qmax, dev)
+    hip = HipEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    timed = {}
+    for name, wsx in (("no_workspace", None), ("position_parts", ws)):
+        for _ in range(3):
+            pkv.prefill_chunk(out, q, *a, kc, vc, qmax, w.scale, wsx)
+        timed[name] = hip.burst_us(sh, lambda i: pkv.prefill_chunk(out, q, *a, kc, vc, qmax, w.scale, wsx),
+                                   max(5, args.steps // 10))
+    spec = ch[0]
+    flops = 4.0 * w.head_dim * w.num_q_heads * sum(range(spec.cached + 1, spec.total + 1))
+    log("prefill, 512 queries over 30000 cached: %.1f us without a workspace, %.1f us with position parts"
+        % (timed["no_workspace"], timed["position_parts"]))
+    return {"workload": "1 chunk of 512 queries over 30000 cached tokens, 32 q / 8 kv heads, head_dim 128, bf16",
+            "algorithmic_gflop": round(flops / 1e9, 3),
+            "kernel_us": {k: round(v, 2) for k, v in timed.items()},
+            "tflops": {k: round(flops / (v * 1e-6) / 1e12, 1) for k, v in timed.items()},
+            "frac_of_bf16_peak": {k: round(flops / (v * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+                                  for k, v in timed.items()}}
 
 
 def cache_ops_leg(dev):

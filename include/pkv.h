@@ -513,7 +513,13 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
                                              int32_t dtype, void* workspace,
                                              size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pkv_paged_attention_prefill_chunk needs (0 if none). */
+/* Workspace bytes pkv_paged_attention_prefill_chunk can use on the current
+ * device (0: none for these sizes). A bf16 call whose row blocks (chunks x
+ * KV heads x ceil(max_q_len / row tokens)) are fewer than the device's CUs
+ * cuts each row block's positions into up to 8 parts, one workgroup each,
+ * when it is given a workspace of this size: the parts leave softmax states
+ * there and a second kernel folds them in part order. total_q and
+ * max_context_len do not change the size. */
 int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_dim, int32_t max_q_len,
                                int32_t max_context_len, size_t* out);
@@ -534,7 +540,12 @@ int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_
  * context_lens: device int32 [num_chunks]. block_table: device int32
  * [num_chunks][max_blocks_per_seq]. max_q_len bounds every chunk's length
  * (rows beyond it are not computed). Chunks with context_lens < q_len are
- * treated as starting at position 0. */
+ * treated as starting at position 0.
+ * workspace: NULL, or device memory of at least
+ * pkv_prefill_workspace_size(...) bytes, 16-byte aligned, no initialisation
+ * needed (smaller gives PKV_ERR_WORKSPACE); with it, a launch with few row
+ * blocks splits their positions over more workgroups (the result differs
+ * only in rounding). Calls that overlap in time must not share a workspace. */
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                                       const int32_t* context_lens, const int32_t* block_table,
                                       const void* k_cache, const void* v_cache,

@@ -20,7 +20,8 @@ from typing import Dict, List, NamedTuple, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["Error", "Allocator", "library", "reshape_and_cache", "copy_blocks",
-           "decode_workspace_size", "decode_workspace", "decode", "prefill_workspace_size", "prefill_chunk",
+           "decode_workspace_size", "decode_workspace", "decode", "prefill_workspace_size",
+           "prefill_workspace", "prefill_chunk",
            "F32", "BF16", "BLOCK_SIZE"]
 
 BLOCK_SIZE = 16
@@ -763,11 +764,22 @@ def prefill_workspace_size(num_chunks: int, total_q: int, num_q_heads: int, num_
     return out.value
 
 
+def prefill_workspace(num_chunks: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      max_q_len: int, device="cuda"):
+    """A prefill workspace (uint8 device tensor) of the size the library asks
+    for, or None when these sizes use none."""
+    torch = _torch()
+    n = prefill_workspace_size(num_chunks, 0, num_q_heads, num_kv_heads, head_dim, max_q_len, 0)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def prefill_chunk(out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache, max_q_len: int,
                   scale: float, workspace=None, stream=None) -> None:
     """Causal chunked-prefill attention; q/out [Tq, Hq, D], cu_q_lens int32
     [C+1], context_lens int32 [C] (including the chunk), block_table int32
-    [C, maxB]."""
+    [C, maxB]. ``workspace`` (``prefill_workspace``): with it, a bf16 call
+    with fewer row blocks than CUs splits their positions over more
+    workgroups."""
     torch = _torch()
     nb, hkv, d = _pool_shape(k_cache)
     if q.dim() != 3 or q.shape[2] != d or tuple(out.shape) != tuple(q.shape):

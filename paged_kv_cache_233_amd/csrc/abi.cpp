@@ -376,7 +376,9 @@ int pkv_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
   if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d", head_dim);
-  *out = 0;
+  (void)total_q;
+  (void)max_context_len;
+  *out = pkv::prefill_workspace_bytes(num_chunks, num_q_heads, num_kv_heads, head_dim, max_q_len);
   return PKV_OK;
 }
 
@@ -388,8 +390,6 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       float scale, int32_t dtype, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   pkv::clear_error();
   if (int e = check_shape(num_kv_heads, head_dim, dtype)) return e;
   if (int e = check_heads(num_q_heads, num_kv_heads)) return e;
@@ -403,9 +403,17 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
   if ((int64_t)num_chunks * num_kv_heads * ((max_q_len + 15) / 16) > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARG, "grid too large");
+  if (workspace != nullptr && dtype == PKV_BF16) {
+    const size_t need =
+        pkv::prefill_workspace_bytes(num_chunks, num_q_heads, num_kv_heads, head_dim, max_q_len);
+    if (workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "prefill workspace %zu bytes, need %zu", workspace_bytes, need);
+    if ((uintptr_t)workspace % 16 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "prefill workspace must be 16-byte aligned");
+  }
   pkv::PrefillArgs a{out, q, cu_q_lens, context_lens, block_table, k_cache, v_cache, num_chunks,
                      total_q, num_blocks, max_blocks_per_seq, max_q_len, num_q_heads,
-                     num_kv_heads, head_dim, scale, dtype};
+                     num_kv_heads, head_dim, scale, dtype, workspace, workspace_bytes};
   hipError_t err = pkv::launch_prefill(a, (hipStream_t)stream);
   return err == hipSuccess ? PKV_OK : pkv::hip_fail(err, "prefill launch");
 }

@@ -102,8 +102,14 @@ struct PrefillArgs {
   int32_t head_dim;
   float scale;
   int32_t dtype;
+  void* workspace;          // optional: the position parts' softmax states
+  size_t workspace_bytes;
 };
 
+// Workspace bytes the bf16 prefill uses to cut row blocks into position
+// parts on the current device (0: this shape runs without).
+size_t prefill_workspace_bytes(int32_t num_chunks, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_q_len);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -431,10 +431,20 @@ __device__ __forceinline__ void lds_barrier() {
 
 struct LdsParams {
   PrefillParams p;
-  int32_t row_blocks;     // workgroups per (chunk, KV head, position part)
+  int32_t row_blocks;     // row blocks per (chunk, KV head)
   int32_t per_xcd;        // workgroups per XCD slot range
   int32_t num_wg;         // real workgroups (the grid may hold a few more)
+  // Position parts: each row block's tiles are cut into `parts` equal runs,
+  // one workgroup each. With parts > 1 a workgroup leaves its rows' softmax
+  // state in `states` (slot = its logical index: NG x (2 + 4 D/16) x 256
+  // floats, value v of group gi and thread t at (gi * kPer + v) * 256 + t)
+  // and prefill_fold_kernel writes the output.
+  int32_t parts;
+  float* states;
 };
+
+// Most position parts per row block.
+constexpr int kMaxParts = 8;
 
 // SPLIT = 1: four waves, each with its own rows, walk all of the
 // workgroup's tiles. SPLIT = 2: eight waves; waves 4..7 take the same rows as
@@ -465,10 +475,13 @@ prefill_lds_kernel(LdsParams lp) {
   const int32_t hw = blockIdx.x;
   const int32_t wg = (hw & 7) * lp.per_xcd + (hw >> 3);
   if (wg >= lp.num_wg) return;
-  const int32_t rb = wg % lp.row_blocks;
-  const int32_t pair = wg / lp.row_blocks;
+  const int32_t part = wg % lp.parts;   // the parts of a row block are consecutive
+  const int32_t rbw = wg / lp.parts;
+  const int32_t rb = rbw % lp.row_blocks;
+  const int32_t pair = rbw / lp.row_blocks;
   const int32_t g = pair % p.num_kv_heads;
   const int32_t ch = pair / p.num_kv_heads;
+  float* const state = lp.parts > 1 ? lp.states + (int64_t)wg * NG * kPer * 256 : nullptr;
 
   const int tid = threadIdx.x;
   // (wave-uniform values are made visibly uniform, so that the decisions
@@ -516,10 +529,16 @@ prefill_lds_kernel(LdsParams lp) {
 
   const int32_t ntiles = lim_wg / kKeys + 1;
   if (lim_wg < 0) {
-    // Empty context: nothing to attend to, zero output.
+    // Empty context: nothing to attend to, zero output (with parts, an
+    // empty state, which the fold turns into zeros).
     if (half != 0) return;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
+      if (lp.parts > 1) {
+        float* d = state + gi * kPer * 256 + htid;
+        for (int v = 0; v < kPer; ++v) d[v * 256] = v == 0 ? kNoMax : 0.f;
+        continue;
+      }
       if (!valid[gi]) continue;
       char* dst = reinterpret_cast<char*>(p.out) + row[gi] * L::kRow;
       for (int b = 16 * kg; b < L::kRow; b += 64) *reinterpret_cast<uint4*>(dst + b) = uint4{0u, 0u, 0u, 0u};
@@ -544,12 +563,16 @@ prefill_lds_kernel(LdsParams lp) {
   const float c = p.scale_log2;
   const float tau_raw = kLazyMax / c;
   const int32_t nblk = lim_wg / 16 + 1;        // blocks any row of this workgroup sees
-  // Tiles of this half: [tbeg, tbeg + tcnt) of [0, ntiles). The first half
-  // has the most tiles; both halves take the same number of steps, the
-  // second one's surplus steps being fully masked.
-  const int32_t steps = (ntiles + SPLIT - 1) / SPLIT;
-  const int32_t tbeg = half * steps;
-  const int32_t tcnt = max(0, min(steps, ntiles - tbeg));
+  // Tiles of this part: [t_lo, t_hi) of [0, ntiles) (possibly none); of
+  // this half: [tbeg, tbeg + tcnt). The first half has the most tiles; both
+  // halves take the same number of steps, the second one's surplus steps
+  // being fully masked.
+  const int32_t span = (ntiles + lp.parts - 1) / lp.parts;
+  const int32_t t_lo = min(ntiles, part * span);
+  const int32_t t_hi = min(ntiles, t_lo + span);
+  const int32_t steps = (t_hi - t_lo + SPLIT - 1) / SPLIT;
+  const int32_t tbeg = t_lo + half * steps;
+  const int32_t tcnt = max(0, min(steps, t_hi - tbeg));
   const int32_t* trow = p.block_table + (int64_t)ch * p.max_blocks;
   const uint32_t block_stride = (uint32_t)p.num_kv_heads * L::kRow * 16;
   const char* kbase = p.k_cache + (int64_t)g * L::kRow * 16;
@@ -634,9 +657,9 @@ prefill_lds_kernel(LdsParams lp) {
     for (int gi = 0; gi < NG; ++gi) {
       const lds_float* d = xs + gi * kPer * 256 + htid;
       const float mb = d[0];
-      // The first half always holds position 0, so its max is a real one;
-      // the second half's may still be kNoMax (nothing visible), which gives
-      // it weight 0.
+      // A half that saw nothing visible still has max kNoMax, which gives it
+      // weight 0 (and a row that saw nothing in either keeps sum 0; the
+      // first half of part 0 always holds position 0).
       const float m = fmaxf(acc.mc[gi], mb);
       const float sa_ = __builtin_amdgcn_exp2f(acc.mc[gi] - m);
       const float sb_ = __builtin_amdgcn_exp2f(mb - m);
@@ -650,6 +673,20 @@ prefill_lds_kernel(LdsParams lp) {
     }
   }
 
+  if (lp.parts > 1) {
+    // a part: the rows' state, for the fold
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      float* d = state + gi * kPer * 256 + htid;
+      d[0] = acc.mc[gi];
+      d[256] = acc.l[gi][0];
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[(2 + 4 * e + i) * 256] = acc.o[gi][e][i];
+    }
+    return;
+  }
   // Lane (n, kg) writes dims 16e + 4kg + 0..3 of its column's row.
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
@@ -660,6 +697,69 @@ prefill_lds_kernel(LdsParams lp) {
     for (int e = 0; e < kE; ++e) {
       bf16x2 v01 = {(__bf16)(acc.o[gi][e][0] * inv), (__bf16)(acc.o[gi][e][1] * inv)};
       bf16x2 v23 = {(__bf16)(acc.o[gi][e][2] * inv), (__bf16)(acc.o[gi][e][3] * inv)};
+      *reinterpret_cast<uint2*>(dst + 32 * e) =
+          uint2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
+    }
+  }
+}
+
+// The fold of a launch with position parts: one workgroup of four waves per
+// row block, each lane the same rows as in prefill_lds_kernel; the parts'
+// states in part order, then the normalised output (zeros for a row with no
+// visible position: an empty context).
+template <int D, int NG>
+__global__ void __launch_bounds__(64 * kWaves)
+prefill_fold_kernel(LdsParams lp) {
+  constexpr int kE = D / 16;
+  constexpr int kPer = 2 + 4 * kE;
+  const PrefillParams& p = lp.p;
+  const int32_t rbw = blockIdx.x;
+  const int32_t rb = rbw % lp.row_blocks;
+  const int32_t pair = rbw / lp.row_blocks;
+  const int32_t g = pair % p.num_kv_heads;
+  const int32_t ch = pair / p.num_kv_heads;
+  const int htid = threadIdx.x;
+  const int wq = __builtin_amdgcn_readfirstlane(htid >> 6);
+  const int lane = htid & 63;
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+  const int32_t G = p.group;
+  const int32_t tpg = p.tokens_per_group;
+  const int32_t q_begin = max(0, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch]));
+  const int32_t q_end = min(p.total_q, __builtin_amdgcn_readfirstlane(p.cu_q_lens[ch + 1]));
+  const int32_t qlen = max(0, min(q_end - q_begin, p.max_q_len));
+  const int32_t wg_tok0 = rb * (kWaves * NG * tpg);
+  if (wg_tok0 >= qlen) return;   // the main kernel left nothing here either
+  const int32_t tok0 = wg_tok0 + wq * NG * tpg;
+  const float* base = lp.states + (int64_t)rbw * lp.parts * NG * kPer * 256 + htid;
+  const int64_t part_stride = (int64_t)NG * kPer * 256;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int32_t tok = tok0 + gi * tpg + n / G;
+    if (!(n < tpg * G && tok < qlen)) continue;
+    const int64_t row = ((int64_t)(q_begin + tok)) * p.num_q_heads + (int64_t)g * G + n % G;
+    const float* d0 = base + gi * kPer * 256;
+    float m = kNoMax;
+    for (int32_t k = 0; k < lp.parts; ++k) m = fmaxf(m, d0[k * part_stride]);
+    float l = 0.f;
+    f32x4 o[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int32_t k = 0; k < lp.parts; ++k) {
+      const float* d = d0 + k * part_stride;
+      const float w = __builtin_amdgcn_exp2f(d[0] - m);
+      l += d[256] * w;
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[e][i] += d[(2 + 4 * e + i) * 256] * w;
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    char* dst = reinterpret_cast<char*>(p.out) + (row * D + 4 * kg) * 2;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      bf16x2 v01 = {(__bf16)(o[e][0] * inv), (__bf16)(o[e][1] * inv)};
+      bf16x2 v23 = {(__bf16)(o[e][2] * inv), (__bf16)(o[e][3] * inv)};
       *reinterpret_cast<uint2*>(dst + 32 * e) =
           uint2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
     }
@@ -704,20 +804,35 @@ hipError_t launch_lds_split(const LdsParams& lp, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Position parts of a launch of `nwg` row blocks: with fewer row blocks than
+// CUs (each then runs one eight-wave workgroup), enough parts to give every
+// CU a workgroup, at most kMaxParts; 1 otherwise.
+int position_parts(int64_t nwg) {
+  const int64_t cus = num_cus();
+  if (nwg <= 0 || nwg >= cus) return 1;
+  return (int)std::min<int64_t>(kMaxParts, cus / nwg);
+}
+
 template <int D, int NG>
-hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream) {
+hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream, float* states) {
   LdsParams lp;
   lp.p = prm;
   const int32_t wg_tokens = kWaves * NG * prm.tokens_per_group;
   lp.row_blocks = (prm.max_q_len + wg_tokens - 1) / wg_tokens;
   const int64_t nwg = (int64_t)lp.row_blocks * prm.num_kv_heads * prm.num_chunks;
-  if (nwg * 64 * kWaves * 2 > INT32_MAX) return hipErrorInvalidConfiguration;
-  lp.num_wg = (int32_t)nwg;
+  if (nwg * kMaxParts * 64 * kWaves * 2 > INT32_MAX) return hipErrorInvalidConfiguration;
+  lp.parts = states != nullptr ? position_parts(nwg) : 1;
+  lp.states = states;
+  lp.num_wg = (int32_t)(nwg * lp.parts);
   lp.per_xcd = (lp.num_wg + 7) / 8;
   // Two waves per SIMD either way: with fewer than two workgroups per CU,
   // each workgroup splits its tiles over two sets of waves.
-  if (nwg < 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 2>(lp, stream);
-  return launch_lds_split<D, NG, 1>(lp, stream);
+  if (lp.num_wg >= 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 1>(lp, stream);
+  hipError_t e = launch_lds_split<D, NG, 2>(lp, stream);
+  if (e != hipSuccess || lp.parts == 1) return e;
+  hipLaunchKernelGGL((prefill_fold_kernel<D, NG>), dim3((uint32_t)nwg), dim3(64 * kWaves), 0, stream,
+                     lp);
+  return hipGetLastError();
 }
 
 template <int DT, int D, int NG>
@@ -729,10 +844,10 @@ hipError_t launch_ng(const PrefillParams& prm, hipStream_t stream) {
 }
 
 template <int DT, int D>
-hipError_t launch(const PrefillParams& prm, hipStream_t stream) {
+hipError_t launch(const PrefillParams& prm, hipStream_t stream, float* states) {
   if constexpr (DT == PKV_BF16) {
-    if (prefill_groups() == 1) return launch_lds<D, 1>(prm, stream);
-    return launch_lds<D, 2>(prm, stream);
+    if (prefill_groups() == 1) return launch_lds<D, 1>(prm, stream, states);
+    return launch_lds<D, 2>(prm, stream, states);
   } else if constexpr (Shape<DT, D>::kRow > 256) {
     // fp32 head_dim 128 keeps one column group (register budget).
     return launch_ng<DT, D, 1>(prm, stream);
@@ -744,6 +859,18 @@ hipError_t launch(const PrefillParams& prm, hipStream_t stream) {
 }  // namespace
 
 namespace pkv {
+
+size_t prefill_workspace_bytes(int32_t num_chunks, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_q_len) {
+  if (num_chunks <= 0 || max_q_len <= 0 || num_kv_heads <= 0 || num_q_heads < num_kv_heads)
+    return 0;
+  const int64_t ng = prefill_groups();
+  const int64_t rows = kWaves * ng * (16 / (num_q_heads / num_kv_heads));
+  const int64_t nwg = (int64_t)num_chunks * num_kv_heads * ((max_q_len + rows - 1) / rows);
+  const int parts = position_parts(nwg);
+  if (parts == 1) return 0;
+  return (size_t)(nwg * parts * ng * (2 + 4 * (head_dim / 16)) * 256 * 4);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   PrefillParams p;
@@ -764,9 +891,18 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.group = a.num_q_heads / a.num_kv_heads;
   p.tokens_per_group = 16 / p.group;
   p.scale_log2 = a.scale * kLog2e;
+  // position parts only with a workspace that holds their states
+  float* states = nullptr;
+  if (a.dtype == PKV_BF16 && a.workspace != nullptr) {
+    const size_t need = prefill_workspace_bytes(a.num_chunks, a.num_q_heads, a.num_kv_heads,
+                                                a.head_dim, a.max_q_len);
+    if (need > 0 && a.workspace_bytes >= need) states = reinterpret_cast<float*>(a.workspace);
+  }
   if (a.dtype == PKV_BF16)
-    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, stream) : launch<PKV_BF16, 64>(p, stream);
-  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream) : launch<PKV_F32, 64>(p, stream);
+    return a.head_dim == 128 ? launch<PKV_BF16, 128>(p, stream, states)
+                             : launch<PKV_BF16, 64>(p, stream, states);
+  return a.head_dim == 128 ? launch<PKV_F32, 128>(p, stream, nullptr)
+                           : launch<PKV_F32, 64>(p, stream, nullptr);
 }
 
 }  // namespace pkv

@@ -63,10 +63,14 @@ class KVCache:
 
 
 def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
-               prefill: bool = True, fused_append: bool = False) -> dict:
+               prefill: bool = True, fused_append: bool = False,
+               prefill_workspace: bool = True) -> dict:
     """``fused_append``: the decode sequences' new tokens are not scattered
     by reshape_and_cache but written by the decode itself (decode_append);
-    the chunks' tokens still go through reshape_and_cache."""
+    the chunks' tokens still go through reshape_and_cache.
+    ``prefill_workspace``: the prefill gets the workspace the library asks
+    for (position parts when the launch has few row blocks; kept as
+    res["prefill_ws"]); False runs it without one."""
     import paged_kv_cache_233_amd as pkv
 
     dt = w.torch_dtype
@@ -149,9 +153,12 @@ def run_native(w: workloads.Workload, device="cuda", keep_pools: bool = True,
         cu = np.cumsum([0] + [x.shape[0] for x in qs]).astype(np.int32)
         q = torch.cat(qs).to(device)
         out = torch.empty_like(q)
+        qmax = int(max(x.shape[0] for x in qs))
+        pws = (pkv.prefill_workspace(len(ch), w.num_q_heads, w.num_kv_heads, w.head_dim, qmax, device)
+               if prefill_workspace else None)
         pkv.prefill_chunk(out, q, torch.from_numpy(cu).to(device), torch.from_numpy(lens).to(device),
-                          torch.from_numpy(table).to(device), kc, vc, int(max(x.shape[0] for x in qs)),
-                          w.scale)
+                          torch.from_numpy(table).to(device), kc, vc, qmax, w.scale, pws)
+        res["prefill_ws"] = pws
         res["prefill"] = out
         res["prefill_table"] = table
         res["prefill_lens"] = lens

@@ -39,7 +39,7 @@ def test_mixed_step_on_two_streams_equals_one(name):
         ready.record(main)
         side.wait_event(ready)
         pkv.prefill_chunk(out_p, q_pf, p_cu, p_lens, p_table, nat["k_cache"], nat["v_cache"], qmax,
-                          w.scale, stream=side)
+                          w.scale, nat["prefill_ws"], stream=side)
         pkv.decode(out_d, q_dec, nat["k_cache"], nat["v_cache"], d_table, d_lens, w.scale, ws,
                    stream=main)
         done = torch.cuda.Event()

@@ -30,11 +30,17 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("ws", [True, False], ids=["workspace", "no-workspace"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_prefill_matches_oracle(name):
+def test_prefill_matches_oracle(name, ws):
+    """Every layout with the workspace (the groups-1, -3 and -8 cases have
+    fewer row blocks than CUs, so their positions are cut into parts) and
+    without."""
+    if not ws and CASES[name]["dtype"] == "f32":
+        pytest.skip("f32 takes no workspace: the other case is the same call")
     w = workloads.custom("pf", 50, [40, 300], chunks=CHUNKS, **CASES[name])
-    _announce("prefill %s" % name)
-    nat = run_native(w)
+    _announce("prefill %s %s" % (name, "workspace" if ws else "no workspace"))
+    nat = run_native(w, prefill_workspace=ws)
     ora = run_oracle(w)
     assert np.array_equal(nat["step_slots"], ora["step_slots"])
     assert np.array_equal(nat["prefill_table"], ora["prefill_table"])
@@ -171,7 +177,8 @@ def test_prefill_index_arrays_in_pinned_host_memory():
     pkv.prefill_chunk(out, q, torch.from_numpy(cu).pin_memory(),
                       torch.from_numpy(nat["prefill_lens"].copy()).pin_memory(),
                       torch.from_numpy(nat["prefill_table"].copy()).pin_memory(),
-                      nat["k_cache"], nat["v_cache"], int(max(s.new_tokens for s in w.chunk_seqs)), w.scale)
+                      nat["k_cache"], nat["v_cache"], int(max(s.new_tokens for s in w.chunk_seqs)), w.scale,
+                      nat["prefill_ws"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), nat["prefill"].view(torch.int16))
 
@@ -219,3 +226,32 @@ def test_prefill_context_beyond_one_round_one_set_of_waves():
     _announce("prefill past one round, one set of waves")
     nat = run_native(w)
     _check_rows_one_by_one(w, nat, "one set")
+
+
+def test_prefill_position_parts():
+    """Few row blocks over long contexts (two 256-query chunks over 20000
+    cached tokens: 128 row blocks, cut into 2 position parts; a 64-query
+    chunk over 9000 beside a 40-query one: 32 row blocks, 8 parts): sampled
+    rows against the oracle, and the call without a workspace (no parts)
+    equal to rounding. Then a chunk with a zero context length among them
+    comes out zero."""
+    for name, chunks in (("pp2", [(20000, 256), (20000, 256)]), ("pp8", [(9000, 64), (300, 40)])):
+        w = workloads.custom(name, 62, [], chunks=chunks, num_q_heads=32, num_kv_heads=8,
+                             head_dim=128, dtype="bf16")
+        _announce("prefill position parts %s" % name)
+        nat = run_native(w)
+        assert nat["prefill_ws"] is not None
+        _check_rows_one_by_one(w, nat, name)
+        plain = run_native(w, prefill_workspace=False)
+        assert_close(nat["prefill"], plain["prefill"].float().cpu().numpy().astype(np.float64), "bf16",
+                     "%s parts vs none" % name)
+    q = torch.cat([w.seq_q(s) for s in w.chunk_seqs]).cuda()
+    cu, lens = nat["prefill_cu"], nat["prefill_lens"]
+    out = torch.full_like(q, float("nan"))
+    pkv.prefill_chunk(out, q, torch.from_numpy(cu).cuda(),
+                      torch.tensor([0, int(lens[1])], dtype=torch.int32, device="cuda"),
+                      torch.from_numpy(nat["prefill_table"]).cuda(), nat["k_cache"], nat["v_cache"], 64,
+                      w.scale, nat["prefill_ws"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[: int(cu[1])].float()) == 0
+    assert torch.equal(out[int(cu[1]):].view(torch.int16), nat["prefill"][int(cu[1]):].view(torch.int16))

@@ -249,6 +249,12 @@ def test_device_entry_points_reject_bad_arguments():
     # prefill: bad head_dim
     assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 1, 4, 1, 1, 8,
                 2, 80, ctypes.c_float(1.0), 1, None, 0, None) == pkv.ERR_UNSUPPORTED
+    # prefill: a bf16 workspace smaller than the position parts need, or misaligned
+    # (1 chunk x 8 KV heads x 1 row block: fewer row blocks than CUs)
+    assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 1, 4, 1, 1, 32,
+                8, 128, ctypes.c_float(1.0), 1, 256, 1, None) == pkv.ERR_WORKSPACE
+    assert _raw("pkv_paged_attention_prefill_chunk", 16, 16, 16, 16, 16, 16, 16, 1, 1, 4, 1, 1, 32,
+                8, 128, ctypes.c_float(1.0), 1, 264, 1 << 30, None) == pkv.ERR_INVALID_ARG
     # stage_copy: zero bytes is a no-op; misaligned, NULL or overlapping ranges are refused
     assert _raw("pkv_stage_copy", 16, 32, 0, None) == 0
     assert _raw("pkv_stage_copy", 16, 40, 8, None) == pkv.ERR_INVALID_ARG
@@ -355,3 +361,21 @@ def test_slot_mapping_check():
         with pytest.raises(pkv.Error) as e:
             pkv.check_slot_mapping(np.array(bad, np.int64), nb)
         assert e.value.code == pkv.ERR_INVALID_ARG and what in e.value.message
+
+
+@pytest.mark.full_library
+def test_prefill_workspace_size():
+    """The prefill asks for a workspace only when its row blocks (chunks x KV
+    heads x row blocks per chunk) are fewer than the CUs: then one softmax
+    state slot per (row block, position part). On a host without a GPU the
+    library takes 256 CUs."""
+    def size(c, qmax, hq=32, hkv=8, d=128):
+        return pkv.prefill_workspace_size(c, 0, hq, hkv, d, qmax, 0)
+
+    # 2 chunks x 8 heads x 16 row blocks (512 queries, 32 per row block) = 256: none
+    assert size(2, 512) == 0 and size(0, 512) == 0
+    # 2 x 8 x 8 = 128 row blocks: 2 parts; 1 x 8 x 2 = 16: 8 parts (the most)
+    groups = size(2, 256) // (128 * 2 * (2 + 4 * 8) * 256 * 4)
+    assert groups in (1, 2) and size(2, 256) == 128 * 2 * groups * (2 + 4 * 8) * 256 * 4
+    assert size(1, 64) == 16 * 8 * groups * (2 + 4 * 8) * 256 * 4
+    assert size(1, 64, d=64) < size(1, 64)
