@@ -516,7 +516,8 @@ int pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const voi
 /* Workspace bytes pkv_paged_attention_prefill_chunk can use on the current
  * device (0: none for these sizes). A bf16 call whose row blocks (chunks x
  * KV heads x ceil(max_q_len / row tokens)) are fewer than the device's CUs
- * cuts each row block's positions into up to 8 parts, one workgroup each,
+ * cuts each row block's positions into parts (enough to keep every CU
+ * busy, at most 16), one workgroup each,
  * when it is given a workspace of this size: the parts leave softmax states
  * there and a second kernel folds them in part order. total_q and
  * max_context_len do not change the size. */

@@ -444,7 +444,7 @@ struct LdsParams {
 };
 
 // Most position parts per row block.
-constexpr int kMaxParts = 8;
+constexpr int kMaxParts = 16;
 
 // SPLIT = 1: four waves, each with its own rows, walk all of the
 // workgroup's tiles. SPLIT = 2: eight waves; waves 4..7 take the same rows as
@@ -804,13 +804,21 @@ hipError_t launch_lds_split(const LdsParams& lp, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Position parts of a launch of `nwg` row blocks: with fewer row blocks than
-// CUs (each then runs one eight-wave workgroup), enough parts to give every
-// CU a workgroup, at most kMaxParts; 1 otherwise.
+// Position parts of a launch of `nwg` row blocks. With fewer row blocks
+// than CUs, as many parts as keep one eight-wave workgroup per CU; if that
+// still leaves a quarter of the CUs idle, enough for two four-wave
+// workgroups per CU instead; at most kMaxParts. 1 with a row block per CU
+// or more (more parts there measured slower).
 int position_parts(int64_t nwg) {
+  if (const char* env = getenv("PKV_PREFILL_PARTS")) {   // tuning override
+    const int v = atoi(env);
+    if (v >= 1 && v <= kMaxParts) return v;
+  }
   const int64_t cus = num_cus();
   if (nwg <= 0 || nwg >= cus) return 1;
-  return (int)std::min<int64_t>(kMaxParts, cus / nwg);
+  int64_t parts = cus / nwg;
+  if (4 * parts * nwg < 3 * cus) parts = (2 * cus + nwg - 1) / nwg;
+  return (int)std::min<int64_t>(kMaxParts, parts);
 }
 
 template <int D, int NG>
@@ -827,8 +835,8 @@ hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream, float* state
   lp.per_xcd = (lp.num_wg + 7) / 8;
   // Two waves per SIMD either way: with fewer than two workgroups per CU,
   // each workgroup splits its tiles over two sets of waves.
-  if (lp.num_wg >= 2 * (int64_t)num_cus()) return launch_lds_split<D, NG, 1>(lp, stream);
-  hipError_t e = launch_lds_split<D, NG, 2>(lp, stream);
+  hipError_t e = lp.num_wg >= 2 * (int64_t)num_cus() ? launch_lds_split<D, NG, 1>(lp, stream)
+                                                      : launch_lds_split<D, NG, 2>(lp, stream);
   if (e != hipSuccess || lp.parts == 1) return e;
   hipLaunchKernelGGL((prefill_fold_kernel<D, NG>), dim3((uint32_t)nwg), dim3(64 * kWaves), 0, stream,
                      lp);

@@ -231,11 +231,14 @@ def test_prefill_context_beyond_one_round_one_set_of_waves():
 def test_prefill_position_parts():
     """Few row blocks over long contexts (two 256-query chunks over 20000
     cached tokens: 128 row blocks, cut into 2 position parts; a 64-query
-    chunk over 9000 beside a 40-query one: 32 row blocks, 8 parts): sampled
+    chunk over 9000 beside a 40-query one: 32 row blocks, 8 parts; three
+    200-query chunks over 5000: 168 row blocks, 4 parts, two workgroups per
+    CU): sampled
     rows against the oracle, and the call without a workspace (no parts)
     equal to rounding. Then a chunk with a zero context length among them
     comes out zero."""
-    for name, chunks in (("pp2", [(20000, 256), (20000, 256)]), ("pp8", [(9000, 64), (300, 40)])):
+    for name, chunks in (("pp4", [(5000, 200)] * 3), ("pp2", [(20000, 256), (20000, 256)]),
+                         ("pp8", [(9000, 64), (300, 40)])):
         w = workloads.custom(name, 62, [], chunks=chunks, num_q_heads=32, num_kv_heads=8,
                              head_dim=128, dtype="bf16")
         _announce("prefill position parts %s" % name)

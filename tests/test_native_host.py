@@ -367,15 +367,18 @@ def test_slot_mapping_check():
 def test_prefill_workspace_size():
     """The prefill asks for a workspace only when its row blocks (chunks x KV
     heads x row blocks per chunk) are fewer than the CUs: then one softmax
-    state slot per (row block, position part). On a host without a GPU the
-    library takes 256 CUs."""
+    state slot per (row block, position part), with as many parts as keep a
+    workgroup per CU, or two per CU where that would leave a quarter of them
+    idle (at most 16). On a host without a GPU the library takes 256 CUs."""
     def size(c, qmax, hq=32, hkv=8, d=128):
         return pkv.prefill_workspace_size(c, 0, hq, hkv, d, qmax, 0)
 
+    slot = 2 * (2 + 4 * 8) * 256 * 4   # two column groups, head_dim 128
     # 2 chunks x 8 heads x 16 row blocks (512 queries, 32 per row block) = 256: none
     assert size(2, 512) == 0 and size(0, 512) == 0
-    # 2 x 8 x 8 = 128 row blocks: 2 parts; 1 x 8 x 2 = 16: 8 parts (the most)
-    groups = size(2, 256) // (128 * 2 * (2 + 4 * 8) * 256 * 4)
-    assert groups in (1, 2) and size(2, 256) == 128 * 2 * groups * (2 + 4 * 8) * 256 * 4
-    assert size(1, 64) == 16 * 8 * groups * (2 + 4 * 8) * 256 * 4
+    # 2 x 8 x 8 = 128 row blocks: 2 parts; 1 x 8 x 2 = 16: 16 parts (the most);
+    # 3 x 8 x 7 = 168: one part would leave 88 CUs idle, so 4 (two per CU)
+    assert size(2, 256) == 128 * 2 * slot
+    assert size(1, 64) == 16 * 16 * slot
+    assert size(3, 200) == 168 * 4 * slot
     assert size(1, 64, d=64) < size(1, 64)
