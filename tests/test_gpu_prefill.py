@@ -258,3 +258,27 @@ def test_prefill_position_parts():
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[: int(cu[1])].float()) == 0
     assert torch.equal(out[int(cu[1]):].view(torch.int16), nat["prefill"][int(cu[1]):].view(torch.int16))
+
+
+def test_prefill_position_parts_rows_beyond_total_q():
+    """bf16 with position parts: cu_q_lens claiming 1000 rows of a 20-row
+    query tensor (64 row blocks, 4 parts each). The fold writes the 20 real
+    rows, matching the oracle, and nothing past them: the output tensor is
+    the middle of a larger buffer whose guard rows keep their NaN bytes."""
+    w = workloads.custom("pfbp", 63, [], chunks=[(10, 20)], num_q_heads=8, num_kv_heads=2,
+                         head_dim=64, dtype="bf16")
+    _announce("prefill position parts, rows past total_q")
+    nat = run_native(w)
+    ora = run_oracle(w)
+    q = w.seq_q(w.chunk_seqs[0]).cuda()
+    buf = torch.full((q.shape[0] + 8,) + tuple(q.shape[1:]), float("nan"), dtype=q.dtype, device="cuda")
+    out = buf[4:4 + q.shape[0]]
+    cu = torch.tensor([0, 1000], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([30], dtype=torch.int32, device="cuda")
+    ws = pkv.prefill_workspace(1, 8, 2, 64, 1000)
+    assert ws is not None
+    pkv.prefill_chunk(out, q, cu, lens, torch.from_numpy(nat["prefill_table"]).cuda(), nat["k_cache"],
+                      nat["v_cache"], 1000, w.scale, ws)
+    torch.cuda.synchronize()
+    assert_close(out, ora["prefill"], "bf16", "rows past total_q with parts")
+    assert torch.isnan(buf[:4].float()).all() and torch.isnan(buf[4 + q.shape[0]:].float()).all()
