@@ -30,14 +30,17 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("ws", [True, False], ids=["workspace", "no-workspace"])
-@pytest.mark.parametrize("name", sorted(CASES))
+# (f32 takes no workspace: one case each)
+LAYOUTS = [(name, ws) for name in sorted(CASES) for ws in (True, False)
+           if ws or CASES[name]["dtype"] != "f32"]
+
+
+@pytest.mark.parametrize("name,ws", LAYOUTS,
+                         ids=["%s-%s" % (n, "workspace" if ws else "no-workspace") for n, ws in LAYOUTS])
 def test_prefill_matches_oracle(name, ws):
     """Every layout with the workspace (the groups-1, -3 and -8 cases have
-    fewer row blocks than CUs, so their positions are cut into parts) and
-    without."""
-    if not ws and CASES[name]["dtype"] == "f32":
-        pytest.skip("f32 takes no workspace: the other case is the same call")
+    fewer row blocks than CUs, so their positions are cut into parts) and,
+    for bf16, without."""
     w = workloads.custom("pf", 50, [40, 300], chunks=CHUNKS, **CASES[name])
     _announce("prefill %s %s" % (name, "workspace" if ws else "no workspace"))
     nat = run_native(w, prefill_workspace=ws)
