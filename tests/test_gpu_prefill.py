@@ -263,6 +263,26 @@ def test_prefill_position_parts():
     assert torch.equal(out[int(cu[1]):].view(torch.int16), nat["prefill"][int(cu[1]):].view(torch.int16))
 
 
+@pytest.mark.parametrize("group,d", [(1, 128), (2, 64), (3, 128), (8, 64), (16, 128)])
+def test_prefill_position_parts_group_sizes(group, d):
+    """Position parts at other group sizes and head dims: a column group
+    holds 16 // G query tokens, so the rows a lane owns, in the attend kernel
+    and in the fold alike, change with G. Two chunks over 2000 and 700 cached
+    tokens (4 to 6 row blocks, 16 parts of 2 to 4 tiles), every row against
+    the oracle and against the call without a workspace."""
+    hkv = 1 if group == 16 else 2
+    w = workloads.custom("ppg%d_%d" % (group, d), 70 + group, [], chunks=[(2000, 24), (700, 5)],
+                         num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=d, dtype="bf16")
+    _announce("prefill position parts, group %d, head_dim %d" % (group, d))
+    nat = run_native(w)
+    assert nat["prefill_ws"] is not None
+    ora = run_oracle(w)
+    assert_close(nat["prefill"], ora["prefill"], "bf16", "parts, group %d" % group)
+    plain = run_native(w, prefill_workspace=False)
+    assert_close(nat["prefill"], plain["prefill"].float().cpu().numpy().astype(np.float64), "bf16",
+                 "parts vs none, group %d" % group)
+
+
 def test_prefill_position_parts_rows_beyond_total_q():
     """bf16 with position parts: cu_q_lens claiming 1000 rows of a 20-row
     query tensor (64 row blocks, 4 parts each). The fold writes the 20 real
