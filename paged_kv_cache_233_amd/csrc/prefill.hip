@@ -703,17 +703,23 @@ prefill_lds_kernel(LdsParams lp) {
   }
 }
 
+// Parts whose states one fold thread loads together.
+constexpr int kFoldBatch = 4;
+
 // The fold of a launch with position parts: one workgroup of four waves per
-// row block, each lane the same rows as in prefill_lds_kernel; the parts'
-// states in part order, then the normalised output (zeros for a row with no
-// visible position: an empty context).
+// (row block, column group), each lane the same rows as in
+// prefill_lds_kernel. The parts' states are folded in part order with the
+// online-softmax rescale (to the larger of the two reference maxima), the
+// loads of kFoldBatch parts issued together; then the normalised output
+// (zeros for a row with no visible position: an empty context).
 template <int D, int NG>
 __global__ void __launch_bounds__(64 * kWaves)
 prefill_fold_kernel(LdsParams lp) {
   constexpr int kE = D / 16;
   constexpr int kPer = 2 + 4 * kE;
   const PrefillParams& p = lp.p;
-  const int32_t rbw = blockIdx.x;
+  const int32_t gi = blockIdx.x % NG;
+  const int32_t rbw = blockIdx.x / NG;
   const int32_t rb = rbw % lp.row_blocks;
   const int32_t pair = rbw / lp.row_blocks;
   const int32_t g = pair % p.num_kv_heads;
@@ -730,39 +736,48 @@ prefill_fold_kernel(LdsParams lp) {
   const int32_t qlen = max(0, min(q_end - q_begin, p.max_q_len));
   const int32_t wg_tok0 = rb * (kWaves * NG * tpg);
   if (wg_tok0 >= qlen) return;   // the main kernel left nothing here either
-  const int32_t tok0 = wg_tok0 + wq * NG * tpg;
-  const float* base = lp.states + (int64_t)rbw * lp.parts * NG * kPer * 256 + htid;
+  const int32_t tok = wg_tok0 + wq * NG * tpg + gi * tpg + n / G;
+  if (!(n < tpg * G && tok < qlen)) return;
+  const int64_t row = ((int64_t)(q_begin + tok)) * p.num_q_heads + (int64_t)g * G + n % G;
   const int64_t part_stride = (int64_t)NG * kPer * 256;
+  const float* d0 = lp.states + (int64_t)rbw * lp.parts * part_stride + gi * kPer * 256 + htid;
+  float m = kNoMax, l = 0.f;
+  f32x4 o[kE];
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int32_t tok = tok0 + gi * tpg + n / G;
-    if (!(n < tpg * G && tok < qlen)) continue;
-    const int64_t row = ((int64_t)(q_begin + tok)) * p.num_q_heads + (int64_t)g * G + n % G;
-    const float* d0 = base + gi * kPer * 256;
-    float m = kNoMax;
-    for (int32_t k = 0; k < lp.parts; ++k) m = fmaxf(m, d0[k * part_stride]);
-    float l = 0.f;
-    f32x4 o[kE];
+  for (int e = 0; e < kE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t k0 = 0; k0 < lp.parts; k0 += kFoldBatch) {
+    float v[kFoldBatch][kPer];
 #pragma unroll
-    for (int e = 0; e < kE; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int32_t k = 0; k < lp.parts; ++k) {
-      const float* d = d0 + k * part_stride;
-      const float w = __builtin_amdgcn_exp2f(d[0] - m);
-      l += d[256] * w;
+    for (int b = 0; b < kFoldBatch; ++b)
+      if (k0 + b < lp.parts) {
+        const float* d = d0 + (k0 + b) * part_stride;
 #pragma unroll
-      for (int e = 0; e < kE; ++e)
+        for (int j = 0; j < kPer; ++j) v[b][j] = d[j * 256];
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[e][i] += d[(2 + 4 * e + i) * 256] * w;
-    }
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    char* dst = reinterpret_cast<char*>(p.out) + (row * D + 4 * kg) * 2;
+    for (int b = 0; b < kFoldBatch; ++b)
+      if (k0 + b < lp.parts) {
+        // (an empty part has reference kNoMax and sum 0: weight 0, or a
+        // factor 1 on another empty state)
+        const float mn = fmaxf(m, v[b][0]);
+        const float so = __builtin_amdgcn_exp2f(m - mn);
+        const float sk = __builtin_amdgcn_exp2f(v[b][0] - mn);
+        l = l * so + v[b][1] * sk;
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      bf16x2 v01 = {(__bf16)(o[e][0] * inv), (__bf16)(o[e][1] * inv)};
-      bf16x2 v23 = {(__bf16)(o[e][2] * inv), (__bf16)(o[e][3] * inv)};
-      *reinterpret_cast<uint2*>(dst + 32 * e) =
-          uint2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
-    }
+        for (int e = 0; e < kE; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[e][i] = o[e][i] * so + v[b][2 + 4 * e + i] * sk;
+        m = mn;
+      }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  char* dst = reinterpret_cast<char*>(p.out) + (row * D + 4 * kg) * 2;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    bf16x2 v01 = {(__bf16)(o[e][0] * inv), (__bf16)(o[e][1] * inv)};
+    bf16x2 v23 = {(__bf16)(o[e][2] * inv), (__bf16)(o[e][3] * inv)};
+    *reinterpret_cast<uint2*>(dst + 32 * e) =
+        uint2{__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23)};
   }
 }
 
@@ -838,8 +853,8 @@ hipError_t launch_lds(const PrefillParams& prm, hipStream_t stream, float* state
   hipError_t e = lp.num_wg >= 2 * (int64_t)num_cus() ? launch_lds_split<D, NG, 1>(lp, stream)
                                                       : launch_lds_split<D, NG, 2>(lp, stream);
   if (e != hipSuccess || lp.parts == 1) return e;
-  hipLaunchKernelGGL((prefill_fold_kernel<D, NG>), dim3((uint32_t)nwg), dim3(64 * kWaves), 0, stream,
-                     lp);
+  hipLaunchKernelGGL((prefill_fold_kernel<D, NG>), dim3((uint32_t)(nwg * NG)), dim3(64 * kWaves), 0,
+                     stream, lp);
   return hipGetLastError();
 }
 
