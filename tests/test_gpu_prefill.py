@@ -283,6 +283,21 @@ def test_prefill_position_parts_group_sizes(group, d):
                  "parts vs none, group %d" % group)
 
 
+@pytest.mark.parametrize("parts", [5, 7, 13])
+def test_prefill_fold_partial_batches(parts, monkeypatch):
+    """The fold loads the parts' states four at a time. Part counts that
+    end on a partial batch after full ones (forced through the library's
+    tuning override, which it reads on every call): two chunks over 3000 and
+    1200 cached tokens, every row against the oracle."""
+    monkeypatch.setenv("PKV_PREFILL_PARTS", str(parts))
+    w = workloads.custom("pfb%d" % parts, 80 + parts, [], chunks=[(3000, 40), (1200, 9)],
+                         num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16")
+    _announce("prefill fold, %d parts" % parts)
+    nat = run_native(w)
+    assert nat["prefill_ws"] is not None
+    assert_close(nat["prefill"], run_oracle(w)["prefill"], "bf16", "%d parts" % parts)
+
+
 def test_prefill_position_parts_rows_beyond_total_q():
     """bf16 with position parts: cu_q_lens claiming 1000 rows of a 20-row
     query tensor (64 row blocks, 4 parts each). The fold writes the 20 real
