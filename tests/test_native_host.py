@@ -382,3 +382,20 @@ def test_prefill_workspace_size():
     assert size(1, 64) == 16 * 16 * slot
     assert size(3, 200) == 168 * 4 * slot
     assert size(1, 64, d=64) < size(1, 64)
+    # head_dim 64: 2 + 4 * 4 floats per lane and column group
+    assert size(1, 64, d=64) == 16 * 16 * (2 * (2 + 4 * 4) * 256 * 4)
+    # a column group holds 16 // G query tokens, so a row block (4 waves x 2
+    # column groups) holds 128 tokens at G = 1 and 8 at G = 16:
+    # 1 x 8 x ceil(200 / 128) = 16 row blocks; 1 x 1 x ceil(24 / 8) = 3
+    assert size(1, 200, hq=8, hkv=8) == 16 * 16 * slot
+    assert size(1, 24, hq=16, hkv=1) == 3 * 16 * slot
+
+
+def test_prefill_workspace_size_follows_the_parts_override(monkeypatch):
+    """The library's tuning override of the part count (read on every
+    call) sizes the workspace as it cuts the launch: 128 row blocks x 5."""
+    monkeypatch.setenv("PKV_PREFILL_PARTS", "5")
+    slot = 2 * (2 + 4 * 8) * 256 * 4
+    assert pkv.prefill_workspace_size(2, 0, 32, 8, 128, 256, 0) == 128 * 5 * slot
+    monkeypatch.setenv("PKV_PREFILL_PARTS", "1")
+    assert pkv.prefill_workspace_size(2, 0, 32, 8, 128, 256, 0) == 0
