@@ -391,6 +391,7 @@ def test_prefill_workspace_size():
     assert size(1, 24, hq=16, hkv=1) == 3 * 16 * slot
 
 
+@pytest.mark.full_library
 def test_prefill_workspace_size_follows_the_parts_override(monkeypatch):
     """The library's tuning override of the part count (read on every
     call) sizes the workspace as it cuts the launch: 128 row blocks x 5."""
